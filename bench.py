@@ -1,0 +1,292 @@
+#!/usr/bin/env python3
+"""Throughput of the int4-g64 grouped MoE layer on one MI355X.
+
+Headline: MoE-layer prefill tokens/s at T=4096 (d=2048, f=512, E=256, top-8
++ 1 shared, Zipf(1.1)-skewed expert load), one moe_layer_forward call per
+step, inputs resident in HBM. Also reported on the same JSON line:
+  roofline      the gate/up grouped GEMM (the dominant kernel): algorithmic
+                FLOP per launch / its mean duration (HIP events on the stream
+                the kernel runs on), against the 2.5 PFLOP/s bf16 dense peak;
+  kernels       every kernel's mean duration and rate;
+  decode        batch-1 decode: 1000 steps through the T=1 path, 32 weight
+                copies rotated so no step re-reads weights from cache, replayed
+                as a HIP graph; algorithmic bytes / time per step;
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
+"""
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
+W4_BYTES_PER_EXPERT = None    # filled from the shapes
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def expert_bytes(d, f):
+    # 3 matrices of d*f weights: 4-bit codes + one bf16 scale and bias per 64 weights
+    return 3 * d * f // 2 + 3 * d * f // 64 * 4
+
+
+def file_hash(path):
+    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+
+
+def traffic_from_profile(kernel_src, launches_key):
+    """HBM bytes per launch measured by rocprofv3 counters, if taken on this kernel source."""
+    p = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(p):
+        return None
+    try:
+        rec = json.load(open(p)).get(launches_key)
+        if rec and rec.get("source_sha") == file_hash(kernel_src):
+            return rec["bytes_per_launch"]
+    except Exception:
+        return None
+    return None
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--decode-steps", type=int, default=1000)
+    ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
+              "build (no multi-GPU path)", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import bit_quantized_grouped_router_amd as M
+    import moe_inputs as G
+
+    if not os.path.exists(M.LIB_PATH):
+        from bit_quantized_grouped_router_amd import build
+        build.build()
+    M.lib()
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    torch.cuda.set_device(0)
+    dev = torch.device("cuda", 0)
+
+    cfg = G.CONFIGS["prefill_t4096_zipf"]
+    T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
+    log(f"[bench] generating {cfg.name}")
+    inp = G.make_layer_inputs(cfg)
+    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
+    logits = torch.from_numpy(inp["logits"]).to(dev)
+    w = M.W4Weights.from_numpy(inp["weights"], device=dev)
+    wc = w.c()
+    dm = M.dims(T, d, f, E, k)
+    ws = torch.empty(M.moe_layer_workspace_bytes(dm), dtype=torch.uint8, device=dev)
+    y = torch.empty((T, d), dtype=torch.float32, device=dev)
+
+    rows = T * (k + 1)
+    flop_gate_up = 2.0 * rows * d * 2 * f
+    flop_down = 2.0 * rows * f * d
+    flop_layer = flop_gate_up + flop_down
+
+    # ---------------------------------------------------------------- headline: whole layer
+    log(f"[bench] layer T={T}: warmup {args.warmup}, timed {args.steps}")
+    for _ in range(args.warmup):
+        M.moe_layer_forward(dm, x, logits, w, y=y, ws=ws, wc=wc)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for _ in range(args.steps):
+        M.moe_layer_forward(dm, x, logits, w, y=y, ws=ws, wc=wc)
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    tok_s = T / (ms_per_step / 1e3)
+    log(f"[bench] layer: {ms_per_step:.3f} ms/step, {tok_s:,.0f} tok/s")
+
+    # ---------------------------------------------------------------- per-kernel timing
+    log("[bench] per-kernel timing with HIP events")
+    ids, wts = M.moe_route(logits, k)
+    perm = M.moe_permute(dm, ids)
+    h, o_r, o_sh = M.moe_expert_ffn_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
+                                       perm["num_tiles"])
+    yk = M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"])
+    torch.cuda.synchronize()
+    nonempty = int((perm["counts"] > 0).sum().item())
+    bytes_layer = ((nonempty + 1) * expert_bytes(d, f) + x.numel() * 2 + logits.numel() * 4
+                   + y.numel() * 4)
+    stream = torch.cuda.current_stream()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    acc = {n: 0.0 for n in names}
+    n_iter = max(args.steps, 5)
+    for it in range(n_iter + 2):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        M.moe_route(logits, k, ids, wts)
+        ev[1].record(stream)
+        M.moe_permute(dm, ids, out=perm)
+        ev[2].record(stream)
+        M.moe_expert_gate_up_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
+                                perm["num_tiles"], h=h)
+        ev[3].record(stream)
+        M.moe_expert_down_w4(dm, h, w, perm["tile_map"], perm["num_tiles"], o_routed=o_r,
+                             o_shared=o_sh)
+        ev[4].record(stream)
+        M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk)
+        ev[5].record(stream)
+        torch.cuda.synchronize()
+        if it >= 2:
+            for i, n in enumerate(names):
+                acc[n] += ev[i].elapsed_time(ev[i + 1]) / n_iter
+    kernels = {}
+    for n in names:
+        us = acc[n] * 1e3
+        kernels[n] = {"us": round(us, 2)}
+    kernels["gate_up"]["TFLOP/s"] = round(flop_gate_up / (acc["gate_up"] / 1e3) / 1e12, 1)
+    kernels["down"]["TFLOP/s"] = round(flop_down / (acc["down"] / 1e3) / 1e12, 1)
+    comb_bytes = T * k * d * 2 + T * d * 4 * 2 + T * k * 8
+    kernels["combine"]["GB/s"] = round(comb_bytes / (acc["combine"] / 1e3) / 1e9, 1)
+    log(f"[bench] kernels: {kernels}")
+    achieved = flop_gate_up / (acc["gate_up"] / 1e3) / 1e12
+    roofline = {"kernel": "gate_up_kernel", "bound": "mfma", "achieved": round(achieved, 2),
+                "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
+                "traffic": traffic_from_profile(
+                    os.path.join(ROOT, "bit_quantized_grouped_router_amd", "csrc", "moe_ffn.hip"),
+                    "gate_up_prefill_t4096_zipf"),
+                "algorithmic_flop_per_launch": flop_gate_up}
+
+    # ---------------------------------------------------------------- decode
+    decode = None
+    if not args.no_decode:
+        dcfg = G.CONFIGS["decode_b1"]
+        n_copies = 32
+        log(f"[bench] decode: {args.decode_steps} steps, {n_copies} weight copies")
+        steps = G.make_decode_steps(dcfg, args.decode_steps)
+        xs = torch.from_numpy(steps["x"].view(np.int16)).to(dev)
+        ls = torch.from_numpy(steps["logits"]).to(dev)
+        wd = M.W4Weights.from_numpy(G.make_weights(dcfg), device=dev)
+        copies = [wd]
+        for _ in range(n_copies - 1):
+            copies.append(M.W4Weights(*[M.W4Matrix(m.codes.clone(), m.scales.clone(),
+                                                   m.biases.clone())
+                                        for m in (wd.w13, wd.w2, wd.s13, wd.s2)]))
+        cstructs = [c.c() for c in copies]
+        dm1 = M.dims(1, dcfg.d, dcfg.f, dcfg.E, dcfg.k)
+        ws1 = torch.empty(M.moe_layer_workspace_bytes(dm1), dtype=torch.uint8, device=dev)
+        yd = torch.empty((args.decode_steps, dcfg.d), dtype=torch.float32, device=dev)
+
+        def run_steps(lo, hi):
+            for s in range(lo, hi):
+                M.moe_layer_forward(dm1, xs[s:s + 1], ls[s:s + 1], None, y=yd[s:s + 1], ws=ws1,
+                                    wc=cstructs[s % n_copies])
+
+        run_steps(0, min(64, args.decode_steps))
+        torch.cuda.synchronize()
+        # stream-launched loop (includes host launch overhead between steps)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record(stream)
+        run_steps(0, args.decode_steps)
+        e1.record(stream)
+        torch.cuda.synchronize()
+        us_stream = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        # the same steps captured as HIP graphs of n_copies steps each
+        us_graph = None
+        try:
+            graphs = []
+            gs = torch.cuda.Stream()
+            chunk = n_copies
+            with torch.cuda.stream(gs):
+                for lo in range(0, args.decode_steps, chunk):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=gs):
+                        run_steps(lo, min(lo + chunk, args.decode_steps))
+                    graphs.append(g)
+            torch.cuda.synchronize()
+            for g in graphs[:2]:
+                g.replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for g in graphs:
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_graph = e0.elapsed_time(e1) * 1e3 / args.decode_steps
+        except Exception as ex:  # graph capture unavailable: keep the stream figure
+            log(f"[bench] decode graph capture failed: {ex}")
+        bytes_step = 9 * expert_bytes(dcfg.d, dcfg.f) + dcfg.d * 2 + dcfg.E * 4 + dcfg.d * 4
+        best = us_graph if us_graph is not None else us_stream
+        decode = {"workload": "decode_b1 (T=1, d=2048, f=512, E=256, top-8 + shared, 1000 steps)",
+                  "bytes_per_step": bytes_step, "us_per_step": round(best, 3),
+                  "GB/s": round(bytes_step / (best * 1e-6) / 1e9, 1),
+                  "frac_hbm": round(bytes_step / (best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+                  "us_per_step_stream_loop": round(us_stream, 3),
+                  "us_per_step_graph": None if us_graph is None else round(us_graph, 3),
+                  "tok/s": round(1e6 / best, 1), "weight_copies": n_copies}
+        log(f"[bench] decode: {decode}")
+        del copies, cstructs
+
+    # ---------------------------------------------------------------- CPU oracle baseline
+    cpu = None
+    if not args.no_cpu_baseline:
+        from oracle import moe_oracle as O
+        try:
+            from threadpoolctl import threadpool_info
+            cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        except Exception:
+            cores = os.cpu_count()
+        n = min(args.cpu_sample_tokens, T)
+        log(f"[bench] CPU oracle on the first {n} tokens")
+        c0 = time.perf_counter()
+        O.layer_forward(inp["x"][:n], inp["logits"][:n], inp["weights"], k, BM=M.moe_block_m())
+        c1 = time.perf_counter()
+        cpu = {"value": round(n / (c1 - c0), 2), "unit": "tok/s", "cores": cores,
+               "kind": "oracle",
+               "sample": f"first {n} of the {T} tokens of {cfg.name}: the whole oracle layer "
+                         f"(route, permute, dequantise every used expert, fp64 FFNs, combine), "
+                         f"{c1 - c0:.1f} s; host cores granted "
+                         f"{len(os.sched_getaffinity(0))}"}
+
+    out = {
+        "metric": "MoE-layer prefill tok/s @T=4096 (% bf16 MFMA peak); decode B=1 HBM GB/s",
+        "value": round(tok_s, 1),
+        "unit": "tok/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16 MFMA, fp32 accumulate, int4-g64 weights",
+        "data": "synthetic (seeded; random int4 codes, bf16 scales U(0.005,0.02), bias -8*scale)",
+        "config": {"workload": "prefill_t4096_zipf: one MoE layer, T=4096, d=2048, f=512, "
+                               "E=256, top-8 + 1 shared expert, Zipf(1.1)-skewed routing",
+                   "T": T, "d": d, "f": f, "E": E, "k": k, "nonempty_experts": int(nonempty)},
+        "layer": {"TFLOP/s": round(flop_layer / (ms_per_step / 1e3) / 1e12, 1),
+                  "frac_bf16_peak": round(flop_layer / (ms_per_step / 1e3) / 1e12
+                                          / PEAK_BF16_TFLOPS, 4),
+                  "algorithmic_bytes": int(bytes_layer),
+                  "GB/s": round(bytes_layer / (ms_per_step / 1e3) / 1e9, 1)},
+        "roofline": roofline,
+        "kernels": kernels,
+        "decode": decode,
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -1,0 +1,137 @@
+// Device-side helpers shared by the gfx950 kernels of the int4-g64 MoE layer.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace moe {
+
+constexpr int kGroup = 64;  // weights per (scale, bias) pair along the input dimension
+constexpr int kWave = 64;   // CDNA wavefront width
+
+typedef __bf16 bf16x8_t __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
+typedef float f32x16_t __attribute__((ext_vector_type(16)));
+typedef float f32x4_t __attribute__((ext_vector_type(4)));
+
+struct W4 {
+  const uint8_t *codes;
+  const uint16_t *scales;
+  const uint16_t *biases;
+};
+
+__device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
+  return __uint_as_float(bits16 << 16);
+}
+
+// Two fp32 values rounded to nearest-even bf16 and packed (a in the low half).
+// On gfx950 this is one v_cvt_pk_bf16_f32.
+__device__ __forceinline__ uint32_t pack_bf16x2(float a, float b) {
+  bf16x2_t v;
+  v[0] = (__bf16)a;
+  v[1] = (__bf16)b;
+  return __builtin_bit_cast(uint32_t, v);
+}
+
+__device__ __forceinline__ uint16_t to_bf16(float a) {
+  return __builtin_bit_cast(uint16_t, (__bf16)a);
+}
+
+// Dequantise eight consecutive columns of one row (one 32-bit word of codes,
+// all in the same 64-column group): w = bf16_rne(fp32(s*q + b)).
+// s*q is exact in fp32, so fmaf rounds exactly once, like a multiply then add.
+// Result: four words of packed bf16 pairs, columns (0,1) (2,3) (4,5) (6,7).
+__device__ __forceinline__ uint4 dequant8(uint32_t c, float s, float b) {
+  const uint32_t lo = c & 0x0F0F0F0Fu;         // even columns: bytes' low nibbles
+  const uint32_t hi = (c >> 4) & 0x0F0F0F0Fu;  // odd columns: bytes' high nibbles
+  uint4 r;
+  r.x = pack_bf16x2(fmaf(s, (float)(lo & 0xFFu), b), fmaf(s, (float)(hi & 0xFFu), b));
+  r.y = pack_bf16x2(fmaf(s, (float)((lo >> 8) & 0xFFu), b), fmaf(s, (float)((hi >> 8) & 0xFFu), b));
+  r.z = pack_bf16x2(fmaf(s, (float)((lo >> 16) & 0xFFu), b), fmaf(s, (float)((hi >> 16) & 0xFFu), b));
+  r.w = pack_bf16x2(fmaf(s, (float)(lo >> 24), b), fmaf(s, (float)(hi >> 24), b));
+  return r;
+}
+
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g / (1.0f + expf(-g)) * u;
+}
+
+// Order-preserving key of a router logit: larger logit -> larger key; -0 and
+// +0 map to the same key; NaN maps below -inf. The low 32 bits hold ~index so
+// that, among equal logits, the lower expert index has the larger key.
+// Every real key is >= 1, so 0 can mark an empty slot.
+__device__ __forceinline__ uint64_t route_key(float v, uint32_t idx) {
+  uint32_t u = __float_as_uint(v);
+  if (u == 0x80000000u) u = 0u;
+  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  if (v != v) ord = 0u;
+  return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+}
+
+// The logit a key was made from (with -0 returned as +0).
+__device__ __forceinline__ float key_logit(uint64_t key) {
+  const uint32_t ord = (uint32_t)(key >> 32);
+  const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
+  return __uint_as_float(u);
+}
+
+__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) {
+    uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
+    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
+    uint64_t o = ((uint64_t)hi << 32) | lo;
+    v = o > v ? o : v;
+  }
+  return v;
+}
+
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int off = 32; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Sum over aligned groups of `width` lanes (width a power of two <= 64).
+template <int width>
+__device__ __forceinline__ float group_sum(float v) {
+#pragma unroll
+  for (int off = width / 2; off >= 1; off >>= 1) v += __shfl_xor(v, off, kWave);
+  return v;
+}
+
+// Top-k over E logits of one token by one wavefront. Lane l holds experts
+// l, l+64, l+128, ... Returns, in lanes 0..k-1, the chosen expert id and its
+// fp32 logit (slot j in lane j), slots ordered by key descending.
+template <int kMaxPerLane>
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int k,
+                                          int *out_id, float *out_logit) {
+  const int lane = threadIdx.x & (kWave - 1);
+  uint64_t key[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) {
+    const int e = lane + i * kWave;
+    key[i] = e < E ? route_key(row[e], (uint32_t)e) : 0ull;
+  }
+  int my_id = 0;
+  float my_logit = 0.f;
+  for (int j = 0; j < k; ++j) {
+    uint64_t best = 0;
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
+    const uint64_t win = wave_max_u64(best);
+    uint32_t id = ~(uint32_t)win;
+    if (id >= (uint32_t)E) id = 0;  // unreachable while k <= E; keeps ids in range
+#pragma unroll
+    for (int i = 0; i < kMaxPerLane; ++i)
+      if (key[i] == win) key[i] = 0;  // keys are unique: exactly one slot holds the winner
+    if (lane == j) {
+      my_id = (int)id;
+      my_logit = key_logit(win);
+    }
+  }
+  *out_id = my_id;
+  *out_logit = my_logit;
+}
+
+}  // namespace moe

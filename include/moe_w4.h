@@ -1,0 +1,223 @@
+/*
+ * moe_w4.h - C ABI of the MI355X (gfx950) int4-g64 grouped MoE expert layer.
+ *
+ * The layer is the one the noticiai.com.br page on Perplexity's Lily engine
+ * describes for Qwen3.6-35B-A3B:
+ *   - section "O modelo em tres formatos de carga": a router scores E = 256
+ *     experts and keeps k = 8 per token; one shared expert sees every token;
+ *   - section "Prefill e decode: onde estao os ganhos": expert weights are
+ *     4-bit affine codes in groups of 64 that share one bf16 scale and one
+ *     bf16 bias; they are rebuilt to bf16 one tile at a time inside the
+ *     grouped GEMM and accumulated in fp32; the routing histogram, prefix
+ *     scan, scatter and block map run on the GPU with no CPU synchronisation
+ *     inside the layer; at batch-1 decode the layer is bandwidth bound.
+ *
+ * Conventions for every entry point
+ *   - Every tensor pointer is a DEVICE pointer, allocated and owned by the
+ *     caller. The library never allocates, frees, copies to the host or
+ *     synchronises. Scratch space comes from a caller workspace.
+ *   - `stream` is a hipStream_t (NULL = the default stream). All work is
+ *     enqueued on it in order and the call returns without waiting.
+ *   - Arguments are validated on the host before anything is enqueued. On a
+ *     failed check a negative moe_status is returned and nothing is enqueued.
+ *     A failed kernel launch returns MOE_E_HIP (moe_last_hip_error() has the
+ *     hipError_t). Faults inside kernels surface at the caller's next sync.
+ *   - T == 0 is valid: the call returns MOE_OK and enqueues nothing.
+ *   - Every pointer must be 16-byte aligned (MOE_E_ALIGN otherwise).
+ *   - Outputs must not alias inputs.
+ *   - No C++ exception crosses this interface. Apart from a thread-local last
+ *     error the library holds no mutable state, so calls on different
+ *     streams or threads are safe when their buffers do not overlap.
+ *   - bf16 tensors are passed as uint16_t bit patterns.
+ *
+ * Shapes (moe_dims)
+ *   T tokens, d hidden size, f expert width (the shared expert has width f
+ *   too), E routed experts, k experts chosen per token.
+ *   Limits: T >= 0, d % 64 == 0, f % 64 == 0, 1 <= k <= min(E, 32),
+ *   1 <= E <= 1024, T*(k+1) < 2^31 and every tensor under 2^31 elements.
+ *
+ * Weight layout (moe_w4_matrix), canonical and unshuffled
+ *   codes  uint8 [n][rows][cols/2]: column c of a row is byte c>>1, in the
+ *          low nibble when c is even and the high nibble when c is odd;
+ *   scales bf16  [n][rows][cols/64]: group j covers columns 64j .. 64j+63;
+ *   biases bf16  [n][rows][cols/64];
+ *   weight w = bf16_rne( fp32( s * q + b ) ), q the unsigned code 0..15.
+ *   Matrices are stored [out][in]: groups run along the input dimension.
+ *
+ * Permuted rows
+ *   The T*k token-expert assignments are sorted by expert (stable in token
+ *   order) into rows 0 .. T*k-1; the shared expert owns rows T*k .. T*k+T-1,
+ *   row T*k+t holding token t. Intermediate tensors h and o are indexed by
+ *   these rows.
+ */
+#ifndef MOE_W4_H
+#define MOE_W4_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  MOE_OK = 0,
+  MOE_E_INVALID = -1,     /* null pointer, negative or inconsistent size */
+  MOE_E_UNSUPPORTED = -2, /* a valid shape outside the limits above */
+  MOE_E_ALIGN = -3,       /* a pointer is not 16-byte aligned */
+  MOE_E_WORKSPACE = -4,   /* workspace smaller than the *_workspace_bytes figure */
+  MOE_E_HIP = -5          /* a HIP call failed; see moe_last_hip_error() */
+} moe_status;
+
+typedef struct {
+  int32_t T; /* tokens */
+  int32_t d; /* hidden size (input of gate/up, output of down) */
+  int32_t f; /* expert intermediate width, routed and shared */
+  int32_t E; /* routed experts */
+  int32_t k; /* experts chosen per token */
+} moe_dims;
+
+typedef struct {
+  const uint8_t *codes;   /* [n][rows][cols/2] packed 4-bit codes */
+  const uint16_t *scales; /* [n][rows][cols/64] bf16 */
+  const uint16_t *biases; /* [n][rows][cols/64] bf16 */
+} moe_w4_matrix;
+
+typedef struct {
+  moe_w4_matrix w13; /* routed gate|up: n = E, rows = 2f (gate rows 0..f-1, up rows f..2f-1), cols = d */
+  moe_w4_matrix w2;  /* routed down:    n = E, rows = d, cols = f */
+  moe_w4_matrix s13; /* shared gate|up: n = 1, rows = 2f, cols = d */
+  moe_w4_matrix s2;  /* shared down:    n = 1, rows = d, cols = f */
+} moe_w4_weights;
+
+/*
+ * moe_route - top-k selection and router weights
+ * (page section "O modelo em tres formatos de carga": score E experts, keep k).
+ *   logits   fp32  [T][E]  router logits
+ *   topk_ids int32 [T][k]  out: chosen experts, by logit descending; equal
+ *                          logits go to the lower expert index; -0 == +0
+ *   topk_w   fp32  [T][k]  out: softmax over the k chosen logits
+ * One wavefront per token. Preconditions (not checked on the device): no NaN
+ * and at least k finite logits per token; if violated, the ids are still k
+ * distinct values in [0, E) and the weights are unspecified.
+ */
+moe_status moe_route(const float *logits, int32_t T, int32_t E, int32_t k,
+                     int32_t *topk_ids, float *topk_w, void *stream);
+
+/* Rows per tile of the block map (the M tile height of the grouped GEMMs). */
+int32_t moe_block_m(void);
+
+/* Upper bound on the number of tiles of the block map; rows of tile_map to allocate. */
+int32_t moe_tile_capacity(const moe_dims *dm);
+
+/* Bytes of scratch workspace moe_permute needs (may be 0). */
+size_t moe_permute_workspace_bytes(const moe_dims *dm);
+
+/*
+ * moe_permute - routing histogram, exclusive prefix scan, stable scatter and
+ * tile block map, all on the device, no host synchronisation
+ * (page section "Prefill e decode: onde estao os ganhos").
+ *   topk_ids     int32 [T][k]         from moe_route
+ *   counts       int32 [E]            out: rows per expert
+ *   offsets      int32 [E+1]          out: exclusive scan, offsets[E] = T*k
+ *   sorted_token int32 [T*k]          out: token of each permuted row
+ *   row_of       int32 [T*k]          out: permuted row of assignment t*k+j
+ *   tile_map     int32 [cap][4]       out: {group, row_begin, row_end, 0} per
+ *                                     tile, cap = moe_tile_capacity(dm);
+ *                                     groups 0..E-1 in order, then the shared
+ *                                     group E (rows T*k .. T*k+T-1); each group
+ *                                     split into ceil(count/BM) tiles of at most
+ *                                     BM = moe_block_m() rows. Entries past
+ *                                     num_tiles are left untouched.
+ *   num_tiles    int32 [1]            out: tiles written
+ *   ws, ws_bytes                      scratch, >= moe_permute_workspace_bytes(dm)
+ * Deterministic: the row order does not depend on scheduling.
+ * Precondition: every id in [0, E) and distinct within a token (as
+ * moe_route produces).
+ */
+moe_status moe_permute(const moe_dims *dm, const int32_t *topk_ids, int32_t *counts,
+                       int32_t *offsets, int32_t *sorted_token, int32_t *row_of,
+                       int32_t *tile_map, int32_t *num_tiles, void *ws, size_t ws_bytes,
+                       void *stream);
+
+/*
+ * moe_expert_gate_up_w4 - grouped gate/up GEMM over the block map with the
+ * int4-g64 dequantisation fused into the tile (bf16 MFMA operands rebuilt in
+ * LDS one K-tile at a time, fp32 accumulation; page section "Prefill e
+ * decode: onde estao os ganhos"), and SiLU(gate)*up in the epilogue.
+ *   x            bf16  [T][d]
+ *   sorted_token int32 [T*k], tile_map, num_tiles from moe_permute
+ *   h            bf16  [T*k+T][f] out: h[p] = bf16(silu(gate_p) * up_p), with
+ *                gate_p = W13_g[0:f] x_t and up_p = W13_g[f:2f] x_t for row p
+ *                of group g carrying token t
+ */
+moe_status moe_expert_gate_up_w4(const moe_dims *dm, const uint16_t *x,
+                                 const moe_w4_weights *w, const int32_t *sorted_token,
+                                 const int32_t *tile_map, const int32_t *num_tiles,
+                                 uint16_t *h, void *stream);
+
+/*
+ * moe_expert_down_w4 - grouped down GEMM, same fused dequantisation.
+ *   h         bf16 [T*k+T][f] from moe_expert_gate_up_w4
+ *   o_routed  bf16 [T*k][d]   out: W2_g h_p for the routed rows (rounded to bf16)
+ *   o_shared  fp32 [T][d]     out: S2 h_p for the shared rows, row T*k+t -> t
+ */
+moe_status moe_expert_down_w4(const moe_dims *dm, const uint16_t *h, const moe_w4_weights *w,
+                              const int32_t *tile_map, const int32_t *num_tiles,
+                              uint16_t *o_routed, float *o_shared, void *stream);
+
+/* moe_expert_ffn_w4 - moe_expert_gate_up_w4 followed by moe_expert_down_w4. */
+moe_status moe_expert_ffn_w4(const moe_dims *dm, const uint16_t *x, const moe_w4_weights *w,
+                             const int32_t *sorted_token, const int32_t *tile_map,
+                             const int32_t *num_tiles, uint16_t *h, uint16_t *o_routed,
+                             float *o_shared, void *stream);
+
+/*
+ * moe_unpermute_combine - weighted unpermute plus the shared expert
+ * (page section "O modelo em tres formatos de carga": the shared expert sees
+ * every token; it is added with weight 1).
+ *   y[t] = o_shared[t] + sum_j topk_w[t][j] * o_routed[row_of[t*k+j]], fp32
+ *   o_routed bf16 [T*k][d], o_shared fp32 [T][d], topk_w fp32 [T][k],
+ *   row_of int32 [T*k], y fp32 [T][d] (out)
+ */
+moe_status moe_unpermute_combine(const moe_dims *dm, const uint16_t *o_routed,
+                                 const float *o_shared, const float *topk_w,
+                                 const int32_t *row_of, float *y, void *stream);
+
+/* Bytes of workspace moe_layer_forward needs for these dims. */
+size_t moe_layer_workspace_bytes(const moe_dims *dm);
+
+/*
+ * moe_layer_forward - the whole layer on one stream with no host sync:
+ * route, permute, gate/up, down, combine (T >= 2), or the batch-1 decode
+ * path (T == 1: routing recomputed on chip, the 9 experts' 4-bit weights
+ * streamed with 128-bit loads; page section "Prefill e decode: onde estao os
+ * ganhos": at batch 1 bandwidth sets the ceiling).
+ *   x      bf16 [T][d]
+ *   logits fp32 [T][E]
+ *   y      fp32 [T][d] out
+ *   ws     >= moe_layer_workspace_bytes(dm) bytes of device scratch
+ */
+moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float *logits,
+                             const moe_w4_weights *w, float *y, void *ws, size_t ws_bytes,
+                             void *stream);
+
+/*
+ * moe_dequant_w4 - rebuild one int4-g64 matrix to bf16 with the same device
+ * arithmetic the GEMM tiles use (for inspection and tests).
+ *   m     one matrix (n = 1) of rows x cols, cols % 64 == 0
+ *   out   bf16 [rows][cols]
+ */
+moe_status moe_dequant_w4(const moe_w4_matrix *m, int32_t rows, int32_t cols, uint16_t *out,
+                          void *stream);
+
+const char *moe_status_string(int32_t status);
+
+/* hipError_t of the last MOE_E_HIP on this thread (0 if none). */
+int32_t moe_last_hip_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* MOE_W4_H */

@@ -44,7 +44,6 @@ import numpy as np
 GROUP = 64
 
 BF16_MAX = (2.0 - 2.0 ** -7) * 2.0 ** 127
-BF16_SUBNORMAL_ULP_EXP = -133   # 2^-126 * 2^-7
 
 
 # --------------------------------------------------------------------------
@@ -61,25 +60,34 @@ def bf16_to_f64(bits: np.ndarray) -> np.ndarray:
 def round_to_bf16_bits(v: np.ndarray) -> np.ndarray:
     """bf16 bit pattern of the nearest bf16 to each value (ties to even).
 
-    bf16 keeps 8 significant bits; below 2^-126 the grid is fixed at 2^-133
-    (subnormals). Magnitudes that round above the largest finite bf16 become
-    infinity. NaN becomes the quiet NaN 0x7FC0.
+    bf16 keeps 8 significant bits (7 stored). In the normal range the fp64
+    significand is rounded at its 45th bit (52 - 7 stored bits), half to even;
+    a carry out of the significand moves into the exponent, as IEEE intends.
+    Below 2^-126 the bf16 grid is fixed at 2^-133 (subnormals) and the value
+    is rounded on that grid instead. Magnitudes that round above the largest
+    finite bf16 become infinity. NaN becomes the quiet NaN 0x7FC0.
     """
-    v = np.asarray(v, dtype=np.float64)
+    v = np.ascontiguousarray(v, dtype=np.float64)
+    bits = v.view(np.uint64)
+    mag = bits & np.uint64(0x7FFFFFFFFFFFFFFF)
+    lsb = (mag >> np.uint64(45)) & np.uint64(1)
+    mag += np.uint64((1 << 44) - 1)
+    mag += lsb
+    mag >>= np.uint64(45)
+    mag <<= np.uint64(45)
+    val = mag.view(np.float64)
     a = np.abs(v)
-    out = np.zeros(v.shape, dtype=np.uint16)
-    finite = np.isfinite(a) & (a > 0)
-    _, ex = np.frexp(a[finite])                  # a = m * 2^ex, m in [0.5, 1)
-    ulp_exp = np.maximum(ex - 8, BF16_SUBNORMAL_ULP_EXP)
-    r = np.rint(np.ldexp(a[finite], -ulp_exp))   # nearest integer, ties to even
-    mag = np.ldexp(r, ulp_exp)
-    with np.errstate(over="ignore"):
-        bits = np.where(mag > BF16_MAX, np.uint32(0x7F800000),
-                        mag.astype(np.float32).view(np.uint32))
-    out[finite] = (bits >> np.uint32(16)).astype(np.uint16)
-    out[np.isinf(a)] = 0x7F80
-    out[np.signbit(v) & ~np.isnan(v)] |= np.uint16(0x8000)
-    out[np.isnan(v)] = 0x7FC0
+    small = a < 2.0 ** -126
+    if small.any():
+        val[small] = np.rint(a[small] * 2.0 ** 133) * 2.0 ** -133
+    over = val > BF16_MAX
+    if over.any():
+        val[over] = np.inf
+    out = (val.astype(np.float32).view(np.uint32) >> np.uint32(16)).astype(np.uint16)
+    out |= ((bits >> np.uint64(48)) & np.uint64(0x8000)).astype(np.uint16)
+    nan = np.isnan(v)
+    if nan.any():
+        out[nan] = 0x7FC0
     return out
 
 

@@ -1,0 +1,66 @@
+"""Helpers of the GPU parity tests: device upload, read-back and the tolerance checks."""
+import sys
+
+import numpy as np
+import torch
+
+import bit_quantized_grouped_router_amd as M
+from oracle import moe_oracle as O
+
+# output tolerance: max |err| <= 2e-2 * RMS(ref), mean |err| <= 2e-3 * RMS(ref)
+Y_MAX_REL_RMS = 2e-2
+Y_MEAN_REL_RMS = 2e-3
+# router weights: fp32 exp/sum/divide against fp64
+W_ABS = 2e-6
+
+
+def say(*a):
+    print(*a, flush=True)
+    sys.stdout.flush()
+
+
+def dev_bits(a: np.ndarray) -> torch.Tensor:
+    """uint16 (bf16 bits) numpy -> int16 device tensor with the same bits."""
+    return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).cuda()
+
+
+def host_bits(t: torch.Tensor) -> np.ndarray:
+    return t.detach().view(torch.int16).cpu().numpy().view(np.uint16)
+
+
+def upload(inp):
+    cfg = inp["cfg"]
+    x = dev_bits(inp["x"])
+    logits = torch.from_numpy(inp["logits"]).cuda()
+    w = M.W4Weights.from_numpy(inp["weights"])
+    dm = M.dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
+    return dm, x, logits, w
+
+
+def check_y(y_gpu: np.ndarray, y_ref: np.ndarray, what: str = "y"):
+    err = np.abs(y_gpu.astype(np.float64) - y_ref)
+    rms = float(np.sqrt(np.mean(y_ref ** 2)))
+    assert np.isfinite(y_gpu).all(), f"{what}: non-finite output"
+    mx, mean = float(err.max()), float(err.mean())
+    say(f"  {what}: rms={rms:.4g} max_err/rms={mx / rms:.3e} mean_err/rms={mean / rms:.3e}")
+    assert mx <= Y_MAX_REL_RMS * rms, f"{what}: max err {mx / rms:.3e} x RMS"
+    assert mean <= Y_MEAN_REL_RMS * rms, f"{what}: mean err {mean / rms:.3e} x RMS"
+    return mx / rms, mean / rms
+
+
+def bf16_ulp(v: np.ndarray) -> np.ndarray:
+    """Spacing of bf16 values at |v| (normal range)."""
+    a = np.maximum(np.abs(v), 2.0 ** -126)
+    return np.exp2(np.floor(np.log2(a)) - 7)
+
+
+def check_bf16_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str, max_frac: float = 0.01):
+    """bf16 tensor vs an oracle (bf16-valued) tensor: every element within one bf16 ulp,
+    and at most max_frac of them not bit-identical."""
+    g = O.bf16_to_f64(gpu_bits)
+    diff = np.abs(g - ref)
+    ulp = bf16_ulp(np.maximum(np.abs(g), np.abs(ref)))
+    frac = float(np.mean(diff > 0))
+    say(f"  {what}: {frac:.2e} of elements differ, max diff {float((diff / ulp).max()):.2f} ulp")
+    assert (diff <= ulp * 1.0000001).all(), f"{what}: difference above one bf16 ulp"
+    assert frac <= max_frac, f"{what}: {frac:.3e} of elements differ"

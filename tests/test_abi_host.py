@@ -1,0 +1,148 @@
+"""The C-ABI library loads, exports every declared entry point, and validates
+arguments on the host before touching the GPU (no GPU needed: every call
+below returns before any HIP call)."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import bit_quantized_grouped_router_amd as M
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "moe_w4.h")
+
+OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP = 0, -1, -2, -3, -4, -5
+
+
+@pytest.fixture(scope="module")
+def L():
+    if not os.path.exists(M.LIB_PATH):
+        from bit_quantized_grouped_router_amd import build
+        build.build()
+    return M.lib()
+
+
+def declared_functions():
+    src = open(HEADER).read()
+    src = re.sub(r"/\*.*?\*/", "", src, flags=re.S)
+    return sorted(set(re.findall(r"\b(moe_[a-z0-9_]+)\s*\(", src)))
+
+
+def test_header_declarations_are_all_exported(L):
+    names = declared_functions()
+    assert len(names) >= 14
+    out = subprocess.run(["nm", "-D", "--defined-only", M.LIB_PATH], capture_output=True,
+                         text=True, check=True).stdout
+    exported = set(l.split()[-1] for l in out.splitlines() if " T " in l)
+    missing = [n for n in names if n not in exported]
+    assert not missing, missing
+    assert set(M.EXPORTS) == set(names)
+    for n in names:
+        getattr(L, n)
+
+
+def test_library_has_gfx950_code_only():
+    out = subprocess.run(["/opt/rocm/bin/roc-obj-ls", M.LIB_PATH], capture_output=True, text=True)
+    if out.returncode != 0:
+        pytest.skip("roc-obj-ls unavailable")
+    assert "gfx950" in out.stdout
+    assert not re.search(r"gfx9[0-4]\d\b", out.stdout.replace("gfx950", ""))
+
+
+def _dims(T=16, d=128, f=64, E=8, k=2):
+    return M.MoeDims(T, d, f, E, k)
+
+
+def test_block_m_and_capacity(L):
+    BM = L.moe_block_m()
+    assert BM == 128
+    for (T, E, k) in [(16, 8, 2), (4096, 256, 8), (16384, 256, 8), (1, 256, 8), (3, 5, 5)]:
+        dm = _dims(T=T, d=2048, f=512, E=E, k=k)
+        tk = T * k
+        routed = min(tk, (tk + min(E, tk) * (BM - 1)) // BM)
+        assert L.moe_tile_capacity(ctypes.byref(dm)) == routed + -(-T // BM)
+
+
+def test_status_strings(L):
+    for st in (OK, INVALID, UNSUPPORTED, ALIGN, WORKSPACE, HIP):
+        assert L.moe_status_string(st)
+    assert L.moe_last_hip_error() == 0
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+def test_route_validation(L):
+    assert L.moe_route(None, 0, 8, 2, None, None, None) == OK          # T == 0: no-op
+    assert L.moe_route(None, 4, 8, 2, FAKE, FAKE, None) == INVALID     # null logits
+    assert L.moe_route(FAKE, 4, 8, 9, FAKE, FAKE, None) == INVALID     # k > E
+    assert L.moe_route(FAKE, 4, 8, 0, FAKE, FAKE, None) == INVALID
+    assert L.moe_route(FAKE, -1, 8, 2, FAKE, FAKE, None) == INVALID
+    assert L.moe_route(FAKE, 4, 2048, 8, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.moe_route(FAKE, 4, 64, 33, FAKE, FAKE, None) == UNSUPPORTED
+    assert L.moe_route(FAKE + 4, 4, 8, 2, FAKE, FAKE, None) == ALIGN
+
+
+def test_dims_validation(L):
+    f = L.moe_layer_workspace_bytes
+    assert f(ctypes.byref(_dims(d=100))) == 0
+    assert f(ctypes.byref(_dims(f=96))) == 0
+    assert f(ctypes.byref(_dims(E=2000))) == 0
+    assert f(ctypes.byref(_dims(k=9))) == 0
+    assert f(ctypes.byref(_dims())) > 0
+    assert L.moe_tile_capacity(ctypes.byref(_dims(d=100))) == -1
+    # workspace grows with T
+    a = f(ctypes.byref(_dims(T=100, d=2048, f=512, E=256, k=8)))
+    b = f(ctypes.byref(_dims(T=200, d=2048, f=512, E=256, k=8)))
+    assert b > a > 0
+
+
+def _weights(base=FAKE):
+    m = M.MoeW4Matrix(base, base, base)
+    return M.MoeW4Weights(m, m, m, m)
+
+
+def test_layer_forward_validation(L):
+    w = _weights()
+    dm = _dims()
+    need = L.moe_layer_workspace_bytes(ctypes.byref(dm))
+    fw = L.moe_layer_forward
+    assert fw(ctypes.byref(_dims(T=0)), None, None, ctypes.byref(w), None, None, 0, None) == OK
+    assert fw(ctypes.byref(_dims(d=100)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
+    assert fw(ctypes.byref(dm), FAKE, FAKE, None, FAKE, FAKE, need, None) == INVALID
+    assert fw(ctypes.byref(dm), None, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == INVALID
+    assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(_weights(FAKE + 2)), FAKE, FAKE, need, None) == ALIGN
+    assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(w), FAKE + 8, FAKE, need, None) == ALIGN
+    assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need - 1, None) == WORKSPACE
+    bad = M.MoeW4Weights(w.w13, w.w2, M.MoeW4Matrix(FAKE, None, FAKE), w.s2)
+    assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(bad), FAKE, FAKE, need, None) == INVALID
+
+
+def test_permute_and_ffn_validation(L):
+    dm = _dims(T=300, d=256, f=128, E=16, k=4)
+    need = L.moe_permute_workspace_bytes(ctypes.byref(dm))
+    assert need == 2 * 16 * 4                     # two blocks of 256 tokens x E counters
+    p = L.moe_permute
+    args = [FAKE] * 7
+    assert p(ctypes.byref(dm), *args, FAKE, need - 4, None) == WORKSPACE
+    assert p(ctypes.byref(dm), None, *args[1:], FAKE, need, None) == INVALID
+    w = _weights()
+    assert L.moe_expert_gate_up_w4(ctypes.byref(dm), FAKE, ctypes.byref(w), FAKE, FAKE, FAKE,
+                                   None, None) == INVALID
+    assert L.moe_expert_down_w4(ctypes.byref(dm), FAKE, ctypes.byref(w), FAKE, FAKE, FAKE + 1,
+                                FAKE, None) == ALIGN
+    assert L.moe_unpermute_combine(ctypes.byref(dm), FAKE, FAKE, FAKE, FAKE, None, None) == INVALID
+    assert L.moe_expert_ffn_w4(ctypes.byref(_dims(T=0)), None, None, None, None, None, None,
+                               None, None, None) == OK
+    m = M.MoeW4Matrix(FAKE, FAKE, FAKE)
+    assert L.moe_dequant_w4(ctypes.byref(m), 4, 100, FAKE, None) == UNSUPPORTED
+    assert L.moe_dequant_w4(ctypes.byref(m), 0, 128, FAKE, None) == OK
+    assert L.moe_dequant_w4(None, 4, 128, FAKE, None) == INVALID
+
+
+def test_binding_refuses_cpu_tensors(L):
+    import torch
+    with pytest.raises(M.MoeError):
+        M.moe_route(torch.zeros((4, 8)), 2)
