@@ -90,6 +90,25 @@ def test_route_permute_bit_exact(cfg):
     assert (p["tile_map"][:n, 3] == 0).all()
 
 
+def _h_slack(cfg, inp, ref):
+    T, k = cfg.T, cfg.k
+    x = O.bf16_to_f64(inp["x"])
+    slack = np.zeros((T * k + T, cfg.f))
+    for g in range(cfg.E + 1):
+        lo, hi = (ref["offsets"][g], ref["offsets"][g + 1]) if g < cfg.E else (T * k, T * k + T)
+        if hi == lo:
+            continue
+        toks = ref["sorted_token"][lo:hi] if g < cfg.E else np.arange(T)
+        W = O.dequant_expert(inp["weights"]["w13"] if g < cfg.E else inp["weights"]["s13"],
+                             g if g < cfg.E else 0)
+        X = x[toks]
+        gate, up = X @ W[:cfg.f].T, X @ W[cfg.f:].T
+        g_abs, u_abs = np.abs(X) @ np.abs(W[:cfg.f]).T, np.abs(X) @ np.abs(W[cfg.f:]).T
+        # |d silu(z)/dz| <= 1.1
+        slack[lo:hi] = 1e-5 * (1.1 * np.abs(up) * g_abs + np.abs(O.silu(gate)) * u_abs)
+    return slack
+
+
 @pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
 def test_expert_ffn_and_combine(cfg):
     say(f"[ffn] {cfg.name}")
@@ -97,12 +116,14 @@ def test_expert_ffn_and_combine(cfg):
     r = staged(cfg)
     T, k = cfg.T, cfg.k
     inp = inputs(cfg)
-    # gate/up + SiLU*up against the oracle's h
+    # gate/up + SiLU*up against the oracle's h; where gate or up cancels, allow the
+    # fp32 accumulation error (relative to the sum of |terms|) to move h
     h = host_bits(r["h"])
-    check_bf16_close(h, ref["h"], "h", max_frac=0.02)
+    check_bf16_close(h, ref["h"], "h", max_frac=0.02, slack=_h_slack(cfg, inp, ref))
     # down GEMM from the GPU's own h: o = W2_g h_p, exact in fp64
     hg = O.bf16_to_f64(h)
     o_ref = np.zeros((T * k + T, cfg.d))
+    o_abs = np.zeros((T * k + T, cfg.d))        # sum of |terms|: scale of fp32 rounding
     for g in range(cfg.E + 1):
         lo, hi = (ref["offsets"][g], ref["offsets"][g + 1]) if g < cfg.E else (T * k, T * k + T)
         if hi == lo:
@@ -110,8 +131,10 @@ def test_expert_ffn_and_combine(cfg):
         W2 = O.dequant_expert(inp["weights"]["w2"] if g < cfg.E else inp["weights"]["s2"],
                               g if g < cfg.E else 0)
         o_ref[lo:hi] = hg[lo:hi] @ W2.T
+        o_abs[lo:hi] = np.abs(hg[lo:hi]) @ np.abs(W2).T
     o_r = host_bits(r["o_r"])[:T * k]
-    check_bf16_close(o_r, O.bf16_round(o_ref[:T * k]), "o_routed", max_frac=0.02)
+    check_bf16_close(o_r, O.bf16_round(o_ref[:T * k]), "o_routed", max_frac=0.02,
+                     slack=1e-5 * o_abs[:T * k])
     o_sh = r["o_sh"].cpu().numpy().astype(np.float64)
     rms = np.sqrt(np.mean(o_ref[T * k:] ** 2))
     assert np.abs(o_sh - o_ref[T * k:]).max() <= 1e-5 * rms
