@@ -65,6 +65,9 @@ def main():
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="also run one plain 256 MiB device-to-device copy (a reference "
+                         "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
@@ -84,6 +87,14 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+
+    if args.calibrate_copy:
+        src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
+        dst = torch.empty_like(src)
+        dst.copy_(src)
+        torch.cuda.synchronize()
+        log(f"[bench] calibration copy: {src.numel() * 4} bytes read and written")
+        del src, dst
 
     cfg = G.CONFIGS["prefill_t4096_zipf"]
     T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
@@ -131,6 +142,9 @@ def main():
     names = ["route", "permute", "gate_up", "down", "combine"]
     acc = {n: 0.0 for n in names}
     n_iter = max(args.steps, 5)
+    # all iterations are enqueued before one synchronisation, so the GPU runs
+    # them back to back and each event pair brackets only its kernels
+    evs = []
     for it in range(n_iter + 2):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record(stream)
@@ -146,10 +160,12 @@ def main():
         ev[4].record(stream)
         M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk)
         ev[5].record(stream)
-        torch.cuda.synchronize()
         if it >= 2:
-            for i, n in enumerate(names):
-                acc[n] += ev[i].elapsed_time(ev[i + 1]) / n_iter
+            evs.append(ev)
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1]) / len(evs)
     kernels = {}
     for n in names:
         us = acc[n] * 1e3

@@ -20,6 +20,16 @@ struct W4 {
   const uint16_t *biases;
 };
 
+// Workgroup barrier ordering LDS only. __syncthreads() also orders global
+// memory, which on gfx9 means waiting for every outstanding global load
+// (vmcnt(0)); this barrier waits for LDS operations only, so loads issued
+// ahead for later K steps stay in flight across it.
+__device__ __forceinline__ void lds_barrier() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+  __builtin_amdgcn_s_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 __device__ __forceinline__ float bf16_to_f32(uint32_t bits16) {
   return __uint_as_float(bits16 << 16);
 }
@@ -50,6 +60,73 @@ __device__ __forceinline__ uint4 dequant8(uint32_t c, float s, float b) {
   r.z = pack_bf16x2(fmaf(s, (float)((lo >> 16) & 0xFFu), b), fmaf(s, (float)((hi >> 16) & 0xFFu), b));
   r.w = pack_bf16x2(fmaf(s, (float)(lo >> 24), b), fmaf(s, (float)(hi >> 24), b));
   return r;
+}
+
+// Per (row, group) constants of the fast dequantisation below.
+struct DqGroup {
+  float s, s16, c0, c1;
+  bool fast;
+};
+
+// The fast path builds each code q as an fp16 1024 + q (or 1024 + 16q) by
+// OR-ing the nibble into the mantissa of 1024.0, and lets one mixed-precision
+// FMA form s*(1024 + q) + (b - 1024 s) = s*q + b. That equals fp32(s*q + b)
+// exactly when b - 1024 s and b - 64 s are exact in fp32 (then the FMA rounds
+// once, like the plain formula): both are sums of two 8-bit significands
+// whose exponents differ by at most 15, i.e. 2^-5 <~ |b|/s <~ 2^21 (or b == +0,
+// or s == 0), with s far from the fp32 range ends. Other groups take the
+// plain path (exactness decides, not speed).
+__device__ __forceinline__ DqGroup dq_prepare(uint32_t sb) {
+  const uint32_t sbits = sb << 16, bbits = sb & 0xFFFF0000u;
+  DqGroup q;
+  q.s = __uint_as_float(sbits);
+  const float b = __uint_as_float(bbits);
+  q.s16 = q.s * 0.0625f;
+  q.c0 = fmaf(-1024.0f, q.s, b);
+  q.c1 = fmaf(-64.0f, q.s, b);
+  const int es = (int)((sbits >> 23) & 0xFFu), eb = (int)((bbits >> 23) & 0xFFu);
+  const int diff = eb - es;
+  const bool s_zero = (sbits & 0x7FFFFFFFu) == 0u, b_zero = (bbits & 0x7FFFFFFFu) == 0u;
+  const bool s_ok = es >= 20 && es <= 230;
+  // b == -0 stays on the plain path: there s*0 + b is -0 for s <= -0, while
+  // the fast form cancels to +0
+  q.fast = bbits != 0x80000000u &&
+           (s_zero || (s_ok && (b_zero || (eb <= 230 && diff >= -5 && diff <= 21))));
+  return q;
+}
+
+typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
+
+// Fast path of dequant8 (see dq_prepare): same result, 17 VALU operations.
+__device__ __forceinline__ uint4 dequant8_fast(uint32_t c, const DqGroup &q) {
+  const uint32_t y = c >> 8;
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, (c & 0x000F000Fu) | 0x64006400u);  // cols 0, 4
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, (c & 0x00F000F0u) | 0x64006400u);  // cols 1, 5
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, (y & 0x000F000Fu) | 0x64006400u);  // cols 2, 6
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, (y & 0x00F000F0u) | 0x64006400u);  // cols 3, 7
+  uint4 r;
+  r.x = pack_bf16x2(fmaf((float)h0[0], q.s, q.c0), fmaf((float)h1[0], q.s16, q.c1));
+  r.y = pack_bf16x2(fmaf((float)h2[0], q.s, q.c0), fmaf((float)h3[0], q.s16, q.c1));
+  r.z = pack_bf16x2(fmaf((float)h0[1], q.s, q.c0), fmaf((float)h1[1], q.s16, q.c1));
+  r.w = pack_bf16x2(fmaf((float)h2[1], q.s, q.c0), fmaf((float)h3[1], q.s16, q.c1));
+  return r;
+}
+
+// 32 consecutive columns of one row (16 bytes of codes, one group), either path.
+__device__ __forceinline__ void dequant32(uint4 c, uint32_t sb, uint4 out[4]) {
+  const DqGroup q = dq_prepare(sb);
+  if (q.fast) {
+    out[0] = dequant8_fast(c.x, q);
+    out[1] = dequant8_fast(c.y, q);
+    out[2] = dequant8_fast(c.z, q);
+    out[3] = dequant8_fast(c.w, q);
+  } else {
+    const float s = bf16_to_f32(sb & 0xFFFFu), b = bf16_to_f32(sb >> 16);
+    out[0] = dequant8(c.x, s, b);
+    out[1] = dequant8(c.y, s, b);
+    out[2] = dequant8(c.z, s, b);
+    out[3] = dequant8(c.w, s, b);
+  }
 }
 
 __device__ __forceinline__ float silu_mul(float g, float u) {

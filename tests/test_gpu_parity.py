@@ -182,7 +182,21 @@ def test_dequant_bit_exact_exhaustive_scales():
         out = host_bits(M.moe_dequant_w4(m))
         ref = O.round_to_bf16_bits(O.dequant(codes, s_bits.reshape(n, 1), biases.reshape(n, 1)))
         nan = np.isnan(O.bf16_to_f64(ref))
-        assert np.array_equal(out[~nan], ref[~nan])
+        bad = np.nonzero((out != ref) & ~nan)
+        for r_, c_ in list(zip(*bad))[:8]:
+            say(f"  mismatch s=0x{s_bits[r_]:04x} b=0x{biases[r_]:04x} q={q[r_, c_]} "
+                f"gpu=0x{out[r_, c_]:04x} ref=0x{ref[r_, c_]:04x}")
+        assert len(bad[0]) == 0, f"{len(bad[0])} mismatching weights"
+    # signed zeros: s in {+0, -0} x b in {+0, -0} and b = -0 with normal scales
+    zs = np.array([0x0000, 0x8000, 0x3C00, 0xBC00, 0x0000, 0x8000], np.uint16)
+    zb = np.array([0x0000, 0x8000, 0x8000, 0x8000, 0x8000, 0x0000], np.uint16)
+    q = np.tile(np.arange(16, dtype=np.uint8), (6, 4))
+    codes = (q[:, 0::2] | (q[:, 1::2] << 4)).astype(np.uint8)
+    m = M.W4Matrix(torch.from_numpy(codes).cuda(), dev_bits(zs.reshape(6, 1)),
+                   dev_bits(zb.reshape(6, 1)))
+    out = host_bits(M.moe_dequant_w4(m))
+    ref = O.round_to_bf16_bits(O.dequant(codes, zs.reshape(6, 1), zb.reshape(6, 1)))
+    assert np.array_equal(out, ref)
 
 
 def test_dequant_matches_oracle_on_layer_weights():
