@@ -133,34 +133,33 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g / (1.0f + expf(-g)) * u;
 }
 
-// Order-preserving key of a router logit: larger logit -> larger key; -0 and
-// +0 map to the same key; NaN maps below -inf. The low 32 bits hold ~index so
-// that, among equal logits, the lower expert index has the larger key.
-// Every real key is >= 1, so 0 can mark an empty slot.
-__device__ __forceinline__ uint64_t route_key(float v, uint32_t idx) {
+// Order-preserving 32-bit key of a router logit: larger logit -> larger key;
+// -0 and +0 map to the same key; NaN maps below -inf (to 1). 0 is never a
+// key, so it marks an empty or already chosen slot.
+__device__ __forceinline__ uint32_t logit_key(float v) {
   uint32_t u = __float_as_uint(v);
   if (u == 0x80000000u) u = 0u;
-  uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
-  if (v != v) ord = 0u;
-  return ((uint64_t)ord << 32) | (uint64_t)(~idx);
+  const uint32_t ord = (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  return v != v ? 1u : ord;
 }
 
-// The logit a key was made from (with -0 returned as +0).
-__device__ __forceinline__ float key_logit(uint64_t key) {
-  const uint32_t ord = (uint32_t)(key >> 32);
+// The logit a key was made from (-0 comes back as +0, NaN as a NaN).
+__device__ __forceinline__ float key_logit(uint32_t ord) {
   const uint32_t u = (ord & 0x80000000u) ? (ord & 0x7FFFFFFFu) : ~ord;
   return __uint_as_float(u);
 }
 
-__device__ __forceinline__ uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off >= 1; off >>= 1) {
-    uint32_t lo = __shfl_xor((uint32_t)v, off, kWave);
-    uint32_t hi = __shfl_xor((uint32_t)(v >> 32), off, kWave);
-    uint64_t o = ((uint64_t)hi << 32) | lo;
-    v = o > v ? o : v;
-  }
-  return v;
+// Maximum of v over the wavefront, in a scalar register. Six DPP steps
+// (lane swaps within quads, mirrors within 8 and 16 lanes, row broadcasts)
+// leave the maximum in lane 63; no LDS traffic.
+__device__ __forceinline__ uint32_t wave_max_u32(uint32_t v) {
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0xb1, 0xf, 0xf, false));   // quad_perm 1,0,3,2
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x4e, 0xf, 0xf, false));   // quad_perm 2,3,0,1
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x141, 0xf, 0xf, false));  // row_half_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x140, 0xf, 0xf, false));  // row_mirror
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x142, 0xa, 0xf, false));  // row_bcast:15
+  v = max(v, (uint32_t)__builtin_amdgcn_update_dpp(0, (int)v, 0x143, 0xc, 0xf, false));  // row_bcast:31
+  return __builtin_amdgcn_readlane(v, 63);
 }
 
 __device__ __forceinline__ float wave_sum(float v) {
@@ -177,34 +176,61 @@ __device__ __forceinline__ float group_sum(float v) {
   return v;
 }
 
-// Top-k over E logits of one token by one wavefront. Lane l holds experts
-// l, l+64, l+128, ... Returns, in lanes 0..k-1, the chosen expert id and its
-// fp32 logit (slot j in lane j), slots ordered by key descending.
+// Top-k over E logits of one token by one wavefront (all 64 lanes active).
+// Lane l holds experts l, l+64, l+128, ... Each of the k rounds takes the
+// largest remaining key: a lane-local maximum, a DPP wavefront maximum, and,
+// only when several lanes hold that same key, a second DPP pass for the
+// lowest expert index among them. Returns, in lanes 0..k-1, the chosen
+// expert (slot j in lane j, keys descending, equal keys by ascending index)
+// and its logit. If fewer than k keys exist (k > E cannot happen), ids stay
+// in [0, E).
 template <int kMaxPerLane>
 __device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int k,
                                           int *out_id, float *out_logit) {
   const int lane = threadIdx.x & (kWave - 1);
-  uint64_t key[kMaxPerLane];
+  // all loads unconditional (clamped index) so they are in flight together
+  float v[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = lane + i * kWave;
-    key[i] = e < E ? route_key(row[e], (uint32_t)e) : 0ull;
+    v[i] = row[e < E ? e : 0];
   }
+  uint32_t key[kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kMaxPerLane; ++i) key[i] = lane + i * kWave < E ? logit_key(v[i]) : 0u;
   int my_id = 0;
   float my_logit = 0.f;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0;
+    // lane-local best: the largest key, the lowest slot among equals
+    uint32_t best = key[0];
+    int bi = 0;
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i) best = key[i] > best ? key[i] : best;
-    const uint64_t win = wave_max_u64(best);
-    uint32_t id = ~(uint32_t)win;
-    if (id >= (uint32_t)E) id = 0;  // unreachable while k <= E; keeps ids in range
+    for (int i = 1; i < kMaxPerLane; ++i)
+      if (key[i] > best) {
+        best = key[i];
+        bi = i;
+      }
+    const uint32_t m = wave_max_u32(best);
+    const uint64_t tied = __builtin_amdgcn_ballot_w64(best == m);
+    int wl;
+    if (__builtin_popcountll(tied) == 1) {
+      wl = __builtin_ctzll(tied);
+    } else {
+      // lowest expert index lane + 64*slot among the lanes holding key m
+      const uint32_t idx = (uint32_t)(lane + kWave * bi);
+      wl = (int)(~wave_max_u32(best == m ? ~idx : 0u) & (kWave - 1));
+    }
+    const int wslot = __builtin_amdgcn_readlane(bi, wl);
+    int id = wl + kWave * wslot;
+    if (id >= E) id = 0;  // unreachable while k <= E; keeps ids in range
+    if (lane == wl) {
 #pragma unroll
-    for (int i = 0; i < kMaxPerLane; ++i)
-      if (key[i] == win) key[i] = 0;  // keys are unique: exactly one slot holds the winner
+      for (int i = 0; i < kMaxPerLane; ++i)
+        if (i == wslot) key[i] = 0u;
+    }
     if (lane == j) {
-      my_id = (int)id;
-      my_logit = key_logit(win);
+      my_id = id;
+      my_logit = key_logit(m);
     }
   }
   *out_id = my_id;
