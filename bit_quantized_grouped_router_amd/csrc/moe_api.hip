@@ -41,6 +41,7 @@ moe_status check_dims(const moe_dims *dm) {
   if (dm->k > dm->E) return MOE_E_INVALID;
   if (dm->d % kGroup != 0 || dm->f % kGroup != 0) return MOE_E_UNSUPPORTED;
   if (dm->E > 1024 || dm->k > 32) return MOE_E_UNSUPPORTED;
+  if (dm->d > kGemmMaxK || dm->f > kGemmMaxK) return MOE_E_UNSUPPORTED;
   const long long rows = (long long)dm->T * (dm->k + 1);
   const long long big = dm->d > 2 * dm->f ? dm->d : 2 * dm->f;
   if (rows * big >= (1ll << 31) || (long long)dm->E * 2 * dm->f * dm->d >= (1ll << 34))

@@ -76,22 +76,33 @@ struct DqGroup {
 // whose exponents differ by at most 15, i.e. 2^-5 <~ |b|/s <~ 2^21 (or b == +0,
 // or s == 0), with s far from the fp32 range ends. Other groups take the
 // plain path (exactness decides, not speed).
-__device__ __forceinline__ DqGroup dq_prepare(uint32_t sb) {
+__device__ __forceinline__ bool dq_fast_ok(uint32_t sb) {
   const uint32_t sbits = sb << 16, bbits = sb & 0xFFFF0000u;
-  DqGroup q;
-  q.s = __uint_as_float(sbits);
-  const float b = __uint_as_float(bbits);
-  q.s16 = q.s * 0.0625f;
-  q.c0 = fmaf(-1024.0f, q.s, b);
-  q.c1 = fmaf(-64.0f, q.s, b);
   const int es = (int)((sbits >> 23) & 0xFFu), eb = (int)((bbits >> 23) & 0xFFu);
   const int diff = eb - es;
   const bool s_zero = (sbits & 0x7FFFFFFFu) == 0u, b_zero = (bbits & 0x7FFFFFFFu) == 0u;
   const bool s_ok = es >= 20 && es <= 230;
   // b == -0 stays on the plain path: there s*0 + b is -0 for s <= -0, while
   // the fast form cancels to +0
-  q.fast = bbits != 0x80000000u &&
-           (s_zero || (s_ok && (b_zero || (eb <= 230 && diff >= -5 && diff <= 21))));
+  return bbits != 0x80000000u &&
+         (s_zero || (s_ok && (b_zero || (eb <= 230 && diff >= -5 && diff <= 21))));
+}
+
+// The constants of the fast path (meaningful when dq_fast_ok holds).
+__device__ __forceinline__ DqGroup dq_consts(uint32_t sb) {
+  DqGroup q;
+  q.s = __uint_as_float(sb << 16);
+  const float b = __uint_as_float(sb & 0xFFFF0000u);
+  q.s16 = q.s * 0.0625f;
+  q.c0 = fmaf(-1024.0f, q.s, b);
+  q.c1 = fmaf(-64.0f, q.s, b);
+  q.fast = true;
+  return q;
+}
+
+__device__ __forceinline__ DqGroup dq_prepare(uint32_t sb) {
+  DqGroup q = dq_consts(sb);
+  q.fast = dq_fast_ok(sb);
   return q;
 }
 
@@ -110,6 +121,54 @@ __device__ __forceinline__ uint4 dequant8_fast(uint32_t c, const DqGroup &q) {
   r.z = pack_bf16x2(fmaf((float)h0[1], q.s, q.c0), fmaf((float)h1[1], q.s16, q.c1));
   r.w = pack_bf16x2(fmaf((float)h2[1], q.s, q.c0), fmaf((float)h3[1], q.s16, q.c1));
   return r;
+}
+
+// Constants of dequant8_fast_r held in registers for the whole kernel: gfx9
+// VOP3 encodings take no literal operand, so v_and_or_b32 needs its masks in
+// registers. The asm makes the values opaque to the compiler, which would
+// otherwise fold them back into two VOP2 operations with literals.
+struct DqRegs {
+  uint32_t m_lo, m_hi;  // 0x000F000F, 0x00F000F0 (scalar registers)
+  uint32_t magic;       // 0x64006400: fp16 1024.0 in both halves (vector register)
+};
+
+__device__ __forceinline__ DqRegs dq_regs() {
+  DqRegs r;
+  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(r.m_lo));
+  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(r.m_hi));
+  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(r.magic));
+  return r;
+}
+
+// (a & m) | o in one VALU operation.
+__device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
+  uint32_t r;
+  asm("v_and_or_b32 %0, %1, %2, %3" : "=v"(r) : "v"(a), "s"(m), "v"(o));
+  return r;
+}
+
+// dequant8_fast with each fp16 operand built by one v_and_or_b32: 17 VALU
+// operations for eight weights (one shift, four and-or, eight mixed FMAs,
+// four packing conversions). Same result as dequant8_fast.
+__device__ __forceinline__ uint4 dequant8_fast_r(uint32_t c, const DqGroup &q, const DqRegs &k) {
+  const uint32_t y = c >> 8;
+  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, and_or(c, k.m_lo, k.magic));  // cols 0, 4
+  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, and_or(c, k.m_hi, k.magic));  // cols 1, 5
+  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, and_or(y, k.m_lo, k.magic));  // cols 2, 6
+  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, and_or(y, k.m_hi, k.magic));  // cols 3, 7
+  uint4 r;
+  r.x = pack_bf16x2(fmaf((float)h0[0], q.s, q.c0), fmaf((float)h1[0], q.s16, q.c1));
+  r.y = pack_bf16x2(fmaf((float)h2[0], q.s, q.c0), fmaf((float)h3[0], q.s16, q.c1));
+  r.z = pack_bf16x2(fmaf((float)h0[1], q.s, q.c0), fmaf((float)h1[1], q.s16, q.c1));
+  r.w = pack_bf16x2(fmaf((float)h2[1], q.s, q.c0), fmaf((float)h3[1], q.s16, q.c1));
+  return r;
+}
+
+// SiLU(g) * u with the hardware exp2 and reciprocal (about 1 ulp each): the
+// product is rounded to bf16 afterwards, so a few fp32 ulps do not matter.
+__device__ __forceinline__ float silu_mul_fast(float g, float u) {
+  const float e = __builtin_amdgcn_exp2f(-1.4426950408889634f * g);
+  return g * __builtin_amdgcn_rcpf(1.0f + e) * u;
 }
 
 // 32 consecutive columns of one row (16 bytes of codes, one group), either path.

@@ -12,29 +12,40 @@
 //     per wavefront);
 //   - the weights never pass through LDS: each lane loads 16 bytes of codes
 //     (32 consecutive input columns of one weight row, one quantisation
-//     group), rebuilds them to bf16 with the VALU and uses them directly as
-//     its MFMA B fragments. Within a K step of 64, lane half h feeds input
-//     columns 32h + 8s .. 32h + 8s + 7 to K slice s; the A fragments are read
-//     with the same column mapping, which only permutes the order of the sum;
-//   - the activation rows go through an LDS double buffer (16 KB per K
-//     step), 16-byte chunks XOR-swizzled by row so that the fragment reads of
-//     8 consecutive rows hit distinct banks; one barrier per K step;
-//   - global loads run two K steps ahead of the MFMAs (activations one step
-//     in registers, codes two steps);
+//     group) with a buffer load whose K offset is a scalar, rebuilds them to
+//     bf16 with the VALU and uses them directly as its MFMA B fragments.
+//     Within a K step of 64, lane half h feeds input columns 32h + 8s ..
+//     32h + 8s + 7 to K slice s; the A fragments are read with the same
+//     column mapping, which only permutes the order of the sum;
+//   - the activation rows go global -> LDS directly (global_load_lds_dwordx4,
+//     no registers), into a ring of three 16 KB stages, two K steps ahead;
+//     16-byte chunks are XOR-swizzled by row so that fragment reads of 8 or
+//     16 consecutive rows hit distinct banks: each lane of a DMA instruction
+//     fetches the chunk that belongs at its (contiguous) LDS slot;
+//   - the scales and biases of the tile's 256 weight rows sit in an LDS
+//     table filled once per tile; whether every group of a wavefront's rows
+//     allows the fast dequantisation is decided there too, so the K loop is
+//     specialised on it and carries no per-step test;
 //   - the grid is sized from the block map's capacity (a host-side bound);
-//     workgroups past num_tiles (read on the device) exit at once, so no
-//     host synchronisation is needed; block ids are remapped so that the
-//     N blocks of one tile, and neighbouring tiles of one expert, run on the
-//     same XCD and share its L2.
+//     workgroups past the device-side tile count exit at once, so no host
+//     synchronisation is needed; work items are spread evenly over the 8
+//     XCDs, neighbouring items (the N blocks of one tile, the tiles of one
+//     expert) on the same XCD so they share its L2.
 #include <type_traits>
 
 #include "moe_launch.h"
 
 namespace moe {
 
-constexpr int kKT = 64;        // K per step: one quantisation group
-constexpr int kWgCols = 256;   // weight rows per workgroup (64 per wavefront)
+constexpr int kKT = 64;                      // K per step: one quantisation group
+constexpr int kWgCols = 256;                 // weight rows per workgroup (64 per wavefront)
+constexpr int kRB = kBlockM / 32;            // 32-row blocks per tile
+constexpr int kStages = 3;                   // activation ring depth
+constexpr int kStageBytes = kBlockM * 128;   // one K step of the tile's rows, bf16
+constexpr int kDma = kBlockM * 8 / 256;      // 16-byte DMA chunks per thread per K step
 constexpr int kXcds = 8;
+
+static_assert(kDma == 4, "the K loop is written for four DMA chunks per thread");
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -52,139 +63,149 @@ __device__ __forceinline__ int xcd_remap(int bid, int active) {
   return (slot < per && logical < active) ? logical : -1;
 }
 
-// Byte offset of 16-byte chunk j (0..7) of row r in a 128-byte-row LDS tile.
-// The chunk is XOR-swizzled with (r % 8) ^ ((r / 8) % 2): any 8 consecutive
-// rows put a given chunk in 8 different bank groups, and so do the even (and
-// the odd) rows among any 16, so 16-byte accesses of 8 or 16 consecutive rows
-// are conflict-free whether the LDS serves 8 or 16 lanes per cycle.
-__device__ __forceinline__ int swz(int r, int j) {
-  return r * 128 + ((j ^ (r & 7) ^ ((r >> 3) & 1)) << 4);
-}
+// s_waitcnt with only the vector-memory counter limited (expcnt and lgkmcnt
+// left at their maxima, which means no wait on them).
+#define MOE_WAIT_VMCNT(n) \
+  __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (0x7 << 4) | (0xF << 8) | (((n) >> 4) << 14))
+
+typedef __attribute__((address_space(3))) void lds_void;
+typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
 // Per-workgroup state of one tile, set up once before the K loop.
 struct TileSetup {
-  const uint16_t *act;       // activation matrix (x for gate/up, h for down)
-  uint32_t a_off[4];         // element offsets of this thread's 4 activation chunks
-  int a_dst0;                // LDS byte offset of chunk 0 (chunk i adds 4096 i)
-  const uint8_t *cbase;      // the expert's codes
-  const uint16_t *sbase, *bbase;
-  uint32_t c_off[2], s_off[2];  // this lane's weight rows, per 32-row block
+  const uint16_t *act;    // activation matrix (x for gate/up, h for down)
+  uint32_t a_off[kDma];   // element offsets (K step 0) of this lane's DMA chunks
+  uint32_t a_lds;         // LDS byte offset of this wavefront's first DMA slot in a stage
+  __amdgpu_buffer_rsrc_t codes;  // the expert's codes
+  uint32_t c_off[2];      // byte offsets of this lane's two weight rows (plus its half)
+  const uint32_t *sbl;    // LDS table [K/64][256] of (scale | bias << 16) per weight row
+  int lr0;                // this lane's table column for block 0 (block 1 adds 32)
   int ksteps;
-  int nrb;                   // active 32-row blocks of the tile (1..4), wave-uniform
-  bool wave_on;              // wave-uniform: this wavefront has weight rows (both blocks:
-                             // f and d are multiples of 64)
+  int nrb;                // active 32-row blocks of the tile (1..kRB), wave-uniform
 };
 
-// K loop of one tile. FULL: all four row blocks active (no per-block branches
-// inside the K step, so the scheduler can interleave dequantisation with MFMAs).
-template <bool FULL>
-__device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t (*lds)[kBlockM * 128],
-                                            f32x16_t (&acc)[4][2]) {
+// K loop of one tile. FULL: all row blocks active (no per-block branches
+// inside the K step). FAST: every group of this wavefront's weight rows
+// takes the fast dequantisation.
+//
+// Order of one K step kt: wait until this wavefront's DMA of stage kt has
+// landed (at most the four DMA chunks of stage kt+1, issued one step later,
+// may still be in flight; code loads issued after them only make the wait
+// stricter), barrier (every wavefront's stage kt is in LDS, and every
+// wavefront is done with stage kt-1), DMA of stage kt+2 into the slot of
+// stage kt-1, code loads for step kt+2, then the four K slices.
+template <bool FULL, bool FAST>
+__device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
+                                            f32x16_t (&acc)[kRB][2]) {
   const int lane = threadIdx.x & 63;
   const int klast = st.ksteps - 1;
-  uint4 ar0, ar1, ar2, ar3;
-  auto load_a = [&](int kt) __attribute__((always_inline)) {
-    const uint16_t *a = st.act + kt * kKT;
-    ar0 = *(const uint4 *)(a + st.a_off[0]);
-    ar1 = *(const uint4 *)(a + st.a_off[1]);
-    ar2 = *(const uint4 *)(a + st.a_off[2]);
-    ar3 = *(const uint4 *)(a + st.a_off[3]);
-  };
-  auto store_a = [&](int buf) __attribute__((always_inline)) {
-    *(uint4 *)(&lds[buf][st.a_dst0]) = ar0;
-    *(uint4 *)(&lds[buf][st.a_dst0 + 4096]) = ar1;
-    *(uint4 *)(&lds[buf][st.a_dst0 + 8192]) = ar2;
-    *(uint4 *)(&lds[buf][st.a_dst0 + 12288]) = ar3;
-  };
-  // codes, scales and biases of two K steps (the one in use and the next, in
-  // flight); the loop is unrolled by two so every slot index is a compile-time
-  // constant (registers, not scratch). Scale and bias stay raw until used, so
-  // no instruction waits on them early. Loads are unconditional: an idle
-  // wavefront reads weight row 0 of its matrix and discards the result.
-  uint4 cr[2][2];
-  uint16_t sr[2][2], br[2][2];
-  auto load_b = [&](int kt, auto SLOT) __attribute__((always_inline)) {
-    constexpr int slot = decltype(SLOT)::value;
-#pragma unroll
-    for (int cb = 0; cb < 2; ++cb) {
-      cr[slot][cb] = *(const uint4 *)(st.cbase + st.c_off[cb] + kt * (kKT / 2));
-      sr[slot][cb] = st.sbase[st.s_off[cb] + kt];
-      br[slot][cb] = st.bbase[st.s_off[cb] + kt];
-    }
-  };
+  const DqRegs dk = dq_regs();
+  // codes of three K steps (in use, and the next two in flight); the loop is
+  // unrolled by three so every slot index is a compile-time constant. Loads
+  // are unconditional: past the last step they re-read the last step, and the
+  // DMA still targets the stage of step kt-1, which no one reads any more.
+  u32x4_t cr[3][2];
   // LDS byte address of this lane's A fragment for K slice 0 and row block 0:
   // slice ks xors its chunk index, row block rb adds rb * 4096 (the swizzle
   // depends on row % 16 only)
   const int lrow = (lane & 31) * 128, lx = (lane & 7) ^ ((lane >> 3) & 1), lh = 4 * (lane >> 5);
-  auto step = [&](int kt, auto SLOT) __attribute__((always_inline)) {
-    constexpr int slot = decltype(SLOT)::value;
-    // A(kt+1) to the other LDS buffer (at the last step: a harmless rewrite of
-    // a buffer no one reads any more), then the loads of A(kt+2) and of the
-    // codes of step kt+1 (into the slot step kt-1 has finished with)
-    store_a((kt + 1) & 1);
-    load_a(min(kt + 2, klast));
-    load_b(min(kt + 1, klast), std::integral_constant<int, slot ^ 1>{});
-    const uint8_t *abuf = lds[kt & 1];
-    const uint32_t sb0 = (uint32_t)sr[slot][0] | ((uint32_t)br[slot][0] << 16);
-    const uint32_t sb1 = (uint32_t)sr[slot][1] | ((uint32_t)br[slot][1] << 16);
-    const DqGroup q0 = dq_prepare(sb0), q1 = dq_prepare(sb1);
-    // one wave-uniform choice per K step: the fast dequantisation when every
-    // lane's groups allow it, else the plain one (exact for every input)
-    const bool all_fast = __builtin_amdgcn_ballot_w64(!(q0.fast && q1.fast)) == 0;
-#pragma unroll
-    for (int ks = 0; ks < 4; ++ks) {
-      const uint32_t w0 = ks == 0 ? cr[slot][0].x : ks == 1 ? cr[slot][0].y : ks == 2 ? cr[slot][0].z : cr[slot][0].w;
-      const uint32_t w1 = ks == 0 ? cr[slot][1].x : ks == 1 ? cr[slot][1].y : ks == 2 ? cr[slot][1].z : cr[slot][1].w;
-      uint4 d0, d1;
-      if (all_fast) {
-        d0 = dequant8_fast(w0, q0);
-        d1 = dequant8_fast(w1, q1);
-      } else {
-        d0 = dequant8(w0, bf16_to_f32(sb0 & 0xFFFFu), bf16_to_f32(sb0 >> 16));
-        d1 = dequant8(w1, bf16_to_f32(sb1 & 0xFFFFu), bf16_to_f32(sb1 >> 16));
-      }
-      const bf16x8_t b0 = __builtin_bit_cast(bf16x8_t, d0);
-      const bf16x8_t b1 = __builtin_bit_cast(bf16x8_t, d1);
-      const uint8_t *aks = abuf + lrow + (((lh + ks) ^ lx) << 4);
-      if (FULL) {
-        // all four A fragments first (one LDS wait), then eight MFMAs
-        bf16x8_t a[4];
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb)
-          a[rb] = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks + rb * 4096));
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b0, acc[rb][0], 0, 0, 0);
-          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[rb], b1, acc[rb][1], 0, 0, 0);
-        }
-      } else {
-#pragma unroll
-        for (int rb = 0; rb < 4; ++rb) {
-          if (rb >= st.nrb) continue;
-          const bf16x8_t a = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks + rb * 4096));
-          acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b0, acc[rb][0], 0, 0, 0);
-          acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b1, acc[rb][1], 0, 0, 0);
-        }
-      }
-    }
-    lds_barrier();
-  };
+  // scale/bias words of the next step (read one step ahead)
+  uint32_t sb0, sb1;
 
-  // prologue: A(0) in LDS, A(1) in registers, codes(0) in flight
-  load_a(0);
-  load_b(0, std::integral_constant<int, 0>{});
-  store_a(0);
-  load_a(min(1, klast));
-  lds_barrier();
-  // whole pairs of steps in the loop (every path through its body is the
-  // same, so the memory wait counters carried around the loop are exact),
-  // then the remaining step if ksteps is odd
-  int kt = 0;
-  for (; kt + 2 <= st.ksteps; kt += 2) {
-    step(kt, std::integral_constant<int, 0>{});
-    step(kt + 1, std::integral_constant<int, 1>{});
+  // activations of K step src_ into ring stage stage_
+#define MOE_DMA(src_, stage_)                                                                \
+  {                                                                                          \
+    const uint16_t *a_ = st.act + (size_t)(src_) * kKT;                                      \
+    uint8_t *s_ = lds + (stage_) * kStageBytes + st.a_lds;                                   \
+    __builtin_amdgcn_global_load_lds(a_ + st.a_off[0], (lds_void *)(s_ + 0 * 4096), 16, 0, 0); \
+    __builtin_amdgcn_global_load_lds(a_ + st.a_off[1], (lds_void *)(s_ + 1 * 4096), 16, 0, 0); \
+    __builtin_amdgcn_global_load_lds(a_ + st.a_off[2], (lds_void *)(s_ + 2 * 4096), 16, 0, 0); \
+    __builtin_amdgcn_global_load_lds(a_ + st.a_off[3], (lds_void *)(s_ + 3 * 4096), 16, 0, 0); \
   }
-  if (kt < st.ksteps) step(kt, std::integral_constant<int, 0>{});
+#define MOE_LOAD_B(kt_, slot_)                                                              \
+  {                                                                                         \
+    cr[slot_][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(       \
+                                                 st.codes, st.c_off[0], (kt_) * (kKT / 2), 0)); \
+    cr[slot_][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(       \
+                                                 st.codes, st.c_off[1], (kt_) * (kKT / 2), 0)); \
+  }
+
+  // one K step; slot_ is a literal (0..2) equal to kt_ % 3
+#define MOE_STEP(kt_, slot_)                                                                 \
+  {                                                                                          \
+    const int ktv_ = (kt_);                                                                  \
+    MOE_WAIT_VMCNT(kDma + 2);                                                                \
+    __builtin_amdgcn_s_barrier();                                                            \
+    /* no LDS access or use of this step's codes moves above the wait and barrier */        \
+    asm volatile("" : "+v"(cr[slot_][0]), "+v"(cr[slot_][1])::"memory");                    \
+    MOE_DMA(min(ktv_ + 2, klast), (ktv_ + 2) % kStages);                                     \
+    MOE_LOAD_B(min(ktv_ + 2, klast), ((slot_) + 2) % 3);                                     \
+    const uint32_t s0_ = sb0, s1_ = sb1;                                                     \
+    {                                                                                        \
+      const int kn_ = min(ktv_ + 1, klast) * kWgCols + st.lr0;                               \
+      sb0 = st.sbl[kn_];                                                                     \
+      sb1 = st.sbl[kn_ + 32];                                                                \
+    }                                                                                        \
+    const uint8_t *abuf_ = lds + (ktv_ % kStages) * kStageBytes;                             \
+    DqGroup q0_, q1_;                                                                        \
+    float ps0_ = 0.f, pb0_ = 0.f, ps1_ = 0.f, pb1_ = 0.f;                                    \
+    if (FAST) {                                                                              \
+      q0_ = dq_consts(s0_);                                                                  \
+      q1_ = dq_consts(s1_);                                                                  \
+    } else {                                                                                 \
+      ps0_ = bf16_to_f32(s0_ & 0xFFFFu), pb0_ = bf16_to_f32(s0_ >> 16);                      \
+      ps1_ = bf16_to_f32(s1_ & 0xFFFFu), pb1_ = bf16_to_f32(s1_ >> 16);                      \
+    }                                                                                        \
+    _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                       \
+      const uint32_t w0_ = cr[slot_][0][ks], w1_ = cr[slot_][1][ks];                         \
+      uint4 d0_, d1_;                                                                        \
+      if (FAST) {                                                                            \
+        d0_ = dequant8_fast_r(w0_, q0_, dk);                                                 \
+        d1_ = dequant8_fast_r(w1_, q1_, dk);                                                 \
+      } else {                                                                               \
+        d0_ = dequant8(w0_, ps0_, pb0_);                                                     \
+        d1_ = dequant8(w1_, ps1_, pb1_);                                                     \
+      }                                                                                      \
+      const bf16x8_t b0_ = __builtin_bit_cast(bf16x8_t, d0_);                                \
+      const bf16x8_t b1_ = __builtin_bit_cast(bf16x8_t, d1_);                                \
+      const uint8_t *aks_ = abuf_ + lrow + (((lh + ks) ^ lx) << 4);                          \
+      _Pragma("unroll") for (int rb = 0; rb < kRB; ++rb) {                                   \
+        if (!FULL && rb >= st.nrb) continue;                                                 \
+        const bf16x8_t a_ = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks_ + rb * 4096)); \
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, b0_, acc[rb][0], 0, 0, 0);  \
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, b1_, acc[rb][1], 0, 0, 0);  \
+      }                                                                                      \
+    }                                                                                        \
+  }
+
+  // prologue: stages 0 and 1 and the codes of steps 0 and 1 in flight, the
+  // scales of step 0 in registers
+  // (issued in the same order as inside the loop, step by step, so that the
+  // compiler's wait counts entering the loop agree with those around it)
+  MOE_DMA(0, 0);
+  MOE_LOAD_B(0, 0);
+  asm volatile("" ::: "memory");
+  MOE_DMA(min(1, klast), 1);
+  MOE_LOAD_B(min(1, klast), 1);
+  asm volatile("" ::: "memory");
+  sb0 = st.sbl[st.lr0];
+  sb1 = st.sbl[st.lr0 + 32];
+  // whole triples of steps in the loop (every path through its body is the
+  // same, so the memory wait counters carried around the loop are exact),
+  // then the one or two remaining steps
+  int kt = 0;
+  for (; kt + 3 <= st.ksteps; kt += 3) {
+    MOE_STEP(kt, 0);
+    MOE_STEP(kt + 1, 1);
+    MOE_STEP(kt + 2, 2);
+  }
+  if (kt < st.ksteps) MOE_STEP(kt, 0);
+  if (kt + 1 < st.ksteps) MOE_STEP(kt + 1, 1);
+  // no DMA may still be writing LDS when the workgroup ends
+  MOE_WAIT_VMCNT(0);
+#undef MOE_STEP
+#undef MOE_DMA
+#undef MOE_LOAD_B
 }
 
 template <int KIND>
@@ -192,8 +213,11 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
     const uint16_t *__restrict__ act, W4 wr, W4 ws, const int32_t *__restrict__ sorted_token,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ num_tiles_p,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32, int T, int d, int f, int E,
-    int k, int grid) {
-  __shared__ __attribute__((aligned(16))) uint8_t lds[2][kBlockM * 128];
+    int k) {
+  // LDS: the activation ring, then the scale/bias table of the tile's 256
+  // weight rows for all K/64 groups (sized by the launch)
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  uint32_t *sbl = (uint32_t *)(smem + kStages * kStageBytes);
 
   // K: input width of the GEMM
   const int K = KIND == kGateUp ? d : f;
@@ -216,71 +240,115 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
   TileSetup st;
   st.act = act;
   st.ksteps = K / kKT;
-  // ---- activation rows: 4 chunks of 16 B per thread per K step. Rows past
-  // the tile's end re-read its last row (their results are never stored), so
-  // every load is unconditional and the wait counters stay exact. Chunk i of
-  // this thread is row (tid >> 3) + 32 i, whose swizzle equals that of row
-  // tid >> 3 (it depends on row % 16 only).
-  st.a_dst0 = swz(tid >> 3, tid & 7);
+  // ---- activation rows. DMA instruction i of wavefront w fills tile rows
+  // 32 i + 8 w .. +7 (1 KB, 16 bytes per lane in lane order); lane l lands in
+  // row r = 32 i + 8 w + l / 8 at 16-byte slot l % 8, which holds logical
+  // chunk (l % 8) ^ (r % 8) ^ ((r / 8) % 2) of the row (the swizzle). Rows
+  // past the tile's end re-read its last row (their results are never
+  // stored), so every load is unconditional.
+  st.a_lds = (uint32_t)wave * 1024u;
+  {
+    const int j = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
 #pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const int p = min(row_begin + (tid >> 3) + 32 * i, row_end - 1);
-    uint32_t row;
-    if (KIND == kGateUp) {
-      int tok = shared ? p - TK : sorted_token[p];
-      tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);  // in range even for malformed routing
-      row = (uint32_t)tok;
-    } else {
-      row = (uint32_t)p;
+    for (int i = 0; i < kDma; ++i) {
+      const int p = min(row_begin + 32 * i + 8 * wave + (lane >> 3), row_end - 1);
+      uint32_t row;
+      if (KIND == kGateUp) {
+        int tok = shared ? p - TK : sorted_token[p];
+        tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);  // in range even for malformed routing
+        row = (uint32_t)tok;
+      } else {
+        row = (uint32_t)p;
+      }
+      st.a_off[i] = row * (uint32_t)K + (uint32_t)j * 8u;
     }
-    st.a_off[i] = row * (uint32_t)K + (uint32_t)(tid & 7) * 8u;
   }
   // ---- this wavefront's two 32-row blocks of weight rows
+  bool wave_on;  // wave-uniform: this wavefront has weight rows (both blocks: f, d % 64 == 0)
   int wrow0, wrow1;
   if (KIND == kGateUp) {
     const int unit = n0 + wave * 32;
-    st.wave_on = unit < f;
+    wave_on = unit < f;
     wrow0 = unit + (lane & 31);          // gate rows
     wrow1 = f + unit + (lane & 31);      // up rows
   } else {
     const int col = n0 + wave * 64;
-    st.wave_on = col < d;
+    wave_on = col < d;
     wrow0 = col + (lane & 31);
     wrow1 = col + 32 + (lane & 31);
   }
   const int nrows_w = KIND == kGateUp ? 2 * f : d;
-  // 32-bit offsets from the expert's base pointers (every matrix set < 4 GiB)
-  st.cbase = W.codes + ex * (size_t)nrows_w * (K / 2);
-  st.sbase = W.scales + ex * (size_t)nrows_w * (K / kGroup);
-  st.bbase = W.biases + ex * (size_t)nrows_w * (K / kGroup);
-  const uint32_t R0 = st.wave_on ? (uint32_t)wrow0 : 0u, R1 = st.wave_on ? (uint32_t)wrow1 : 0u;
+  const uint32_t R0 = wave_on ? (uint32_t)wrow0 : 0u, R1 = wave_on ? (uint32_t)wrow1 : 0u;
+  st.codes = __builtin_amdgcn_make_buffer_rsrc((void *)(W.codes + ex * (size_t)nrows_w * (K / 2)),
+                                               (short)0, nrows_w * (K / 2), 0x00020000);
   st.c_off[0] = R0 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
   st.c_off[1] = R1 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
-  st.s_off[0] = R0 * (uint32_t)(K / kGroup);
-  st.s_off[1] = R1 * (uint32_t)(K / kGroup);
-  const int rows = row_end - row_begin;
-  st.nrb = st.wave_on ? (rows + 31) / 32 : 0;
-
-  f32x16_t acc[4][2];
+  // ---- the scale/bias table: lane l of wavefront w fills column 64 w + l,
+  // which is weight row R0 (l < 32) or R1 (l >= 32) of lane l % 32, for all
+  // groups; the wavefront reads back only its own columns. The same pass
+  // decides whether all of them allow the fast dequantisation.
+  st.sbl = sbl;
+  st.lr0 = wave * 64 + (lane & 31);
+  bool fast_ok = true;
+  {
+    const uint32_t R = (lane >> 5) ? R1 : R0;
+    const int ng = K / kGroup;
+    const size_t srow = (ex * (size_t)nrows_w + R) * (size_t)ng;
+    const uint16_t *sp = W.scales + srow, *bp = W.biases + srow;
+    uint32_t *col = sbl + wave * 64 + lane;
+    if (ng % 8 == 0) {
+      // 16-byte loads: each row starts 16-byte aligned (ng * 2 bytes per row)
+      for (int g0 = 0; g0 < ng; g0 += 8) {
+        const uint4 sv = *(const uint4 *)(sp + g0), bv = *(const uint4 *)(bp + g0);
+        const uint32_t su[4] = {sv.x, sv.y, sv.z, sv.w}, bu[4] = {bv.x, bv.y, bv.z, bv.w};
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
-  if (st.nrb == 4)
-    gemm_k_loop<true>(st, lds, acc);
-  else
-    gemm_k_loop<false>(st, lds, acc);
+        for (int q = 0; q < 4; ++q) {
+          const uint32_t w0 = (su[q] & 0xFFFFu) | (bu[q] << 16);
+          const uint32_t w1 = (su[q] >> 16) | (bu[q] & 0xFFFF0000u);
+          col[(g0 + 2 * q) * kWgCols] = w0;
+          col[(g0 + 2 * q + 1) * kWgCols] = w1;
+          fast_ok &= dq_fast_ok(w0) & dq_fast_ok(w1);
+        }
+      }
+    } else {
+      for (int g0 = 0; g0 < ng; ++g0) {
+        const uint32_t w0 = (uint32_t)sp[g0] | ((uint32_t)bp[g0] << 16);
+        col[g0 * kWgCols] = w0;
+        fast_ok &= dq_fast_ok(w0);
+      }
+    }
+  }
+  const bool fast = __builtin_amdgcn_ballot_w64(!fast_ok) == 0;  // wave-uniform
+  const int rows = row_end - row_begin;
+  st.nrb = wave_on ? (rows + 31) / 32 : 0;
+
+  f32x16_t acc[kRB][2];
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
+  if (st.nrb == kRB) {
+    if (fast)
+      gemm_k_loop<true, true>(st, smem, acc);
+    else
+      gemm_k_loop<true, false>(st, smem, acc);
+  } else {
+    if (fast)
+      gemm_k_loop<false, true>(st, smem, acc);
+    else
+      gemm_k_loop<false, false>(st, smem, acc);
+  }
 
   // epilogue; C layout of the 32x32 MFMA: lane l holds column l%32, register
   // r holds row 8*(r/4) + 4*(l/32) + r%4
-  if (!st.wave_on) return;
+  if (!wave_on) return;
 #pragma unroll
-  for (int rb = 0; rb < 4; ++rb) {
+  for (int rb = 0; rb < kRB; ++rb) {
     if (rb >= st.nrb) continue;
 #pragma unroll
     for (int r = 0; r < 16; ++r) {
       const int p = row_begin + rb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
       if (p >= row_end) continue;
       if (KIND == kGateUp) {
-        out_bf16[(size_t)p * f + wrow0] = to_bf16(silu_mul(acc[rb][0][r], acc[rb][1][r]));
+        out_bf16[(size_t)p * f + wrow0] = to_bf16(silu_mul_fast(acc[rb][0][r], acc[rb][1][r]));
       } else if (shared) {
         out_f32[(size_t)(p - TK) * d + wrow0] = acc[rb][0][r];
         out_f32[(size_t)(p - TK) * d + wrow1] = acc[rb][1][r];
@@ -294,25 +362,47 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
 
 static int round_up8(long long n) { return (int)((n + kXcds - 1) / kXcds * kXcds); }
 
+// LDS of one GEMM workgroup for input width K: the activation ring and the
+// scale/bias table (K/64 groups x 256 weight rows x 4 bytes).
+static size_t gemm_lds_bytes(int K) {
+  return (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
+}
+
+// More than 64 KB of dynamic LDS needs a per-kernel opt-in (once per process).
+static hipError_t gemm_setup() {
+  static const hipError_t st = [] {
+    const int max_lds = (int)gemm_lds_bytes(kGemmMaxK);
+    hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_w4_kernel<kGateUp>,
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    if (e == hipSuccess)
+      e = hipFuncSetAttribute((const void *)grouped_gemm_w4_kernel<kDown>,
+                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    return e;
+  }();
+  return st;
+}
+
 hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
                           const int32_t *sorted_token, const int32_t *tile_map,
                           const int32_t *num_tiles, uint16_t *h, hipStream_t s) {
+  if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.f + kWgCols / 2 - 1) / (kWgCols / 2);
   const int grid = round_up8((long long)tile_capacity(dm) * nblk);
-  grouped_gemm_w4_kernel<kGateUp><<<grid, 256, 0, s>>>(x, w.w13, w.s13, sorted_token, tile_map,
-                                                       num_tiles, h, nullptr, dm.T, dm.d, dm.f,
-                                                       dm.E, dm.k, grid);
+  grouped_gemm_w4_kernel<kGateUp><<<grid, 256, gemm_lds_bytes(dm.d), s>>>(
+      x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
+      dm.k);
   return hipGetLastError();
 }
 
 hipError_t launch_down(const Dims &dm, const uint16_t *h, const Weights &w,
                        const int32_t *tile_map, const int32_t *num_tiles, uint16_t *o_routed,
                        float *o_shared, hipStream_t s) {
+  if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.d + kWgCols - 1) / kWgCols;
   const int grid = round_up8((long long)tile_capacity(dm) * nblk);
-  grouped_gemm_w4_kernel<kDown><<<grid, 256, 0, s>>>(h, w.w2, w.s2, nullptr, tile_map, num_tiles,
-                                                     o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
-                                                     dm.k, grid);
+  grouped_gemm_w4_kernel<kDown><<<grid, 256, gemm_lds_bytes(dm.f), s>>>(
+      h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
+      dm.k);
   return hipGetLastError();
 }
 

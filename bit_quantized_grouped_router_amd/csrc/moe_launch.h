@@ -12,6 +12,10 @@ namespace moe {
 
 // Rows per tile of the block map, shared by both grouped GEMMs.
 constexpr int kBlockM = 128;
+// Largest input width of a grouped GEMM: a tile keeps the scales and biases
+// of its 256 weight rows for all K/64 groups in LDS, next to 64 KB of
+// activation buffers (1 KB per group, 160 KB of LDS per CU).
+constexpr int kGemmMaxK = 6144;
 // Tokens per block of the permutation pipeline.
 constexpr int kPermTokens = 256;
 

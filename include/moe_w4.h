@@ -33,8 +33,9 @@
  * Shapes (moe_dims)
  *   T tokens, d hidden size, f expert width (the shared expert has width f
  *   too), E routed experts, k experts chosen per token.
- *   Limits: T >= 0, d % 64 == 0, f % 64 == 0, 1 <= k <= min(E, 32),
- *   1 <= E <= 1024, T*(k+1) < 2^31 and every tensor under 2^31 elements.
+ *   Limits: T >= 0, d % 64 == 0, f % 64 == 0, d <= 6144, f <= 6144,
+ *   1 <= k <= min(E, 32), 1 <= E <= 1024, T*(k+1) < 2^31 and every tensor
+ *   under 2^31 elements.
  *
  * Weight layout (moe_w4_matrix), canonical and unshuffled
  *   codes  uint8 [n][rows][cols/2]: column c of a row is byte c>>1, in the

@@ -111,6 +111,9 @@ def test_layer_forward_validation(L):
     fw = L.moe_layer_forward
     assert fw(ctypes.byref(_dims(T=0)), None, None, ctypes.byref(w), None, None, 0, None) == OK
     assert fw(ctypes.byref(_dims(d=100)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
+    # the grouped GEMMs keep a tile's scales for every K group in LDS: K <= 6144
+    assert fw(ctypes.byref(_dims(d=6208)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
+    assert fw(ctypes.byref(_dims(f=6208)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
     assert fw(ctypes.byref(dm), FAKE, FAKE, None, FAKE, FAKE, need, None) == INVALID
     assert fw(ctypes.byref(dm), None, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == INVALID
     assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(_weights(FAKE + 2)), FAKE, FAKE, need, None) == ALIGN

@@ -123,7 +123,7 @@ def test_small_decode_shapes():
         dm, x, logits, w = upload(inp)
         y = M.moe_layer_forward(dm, x, logits, w)
         torch.cuda.synchronize()
-        ref = O.layer_forward(inp["x"], inp["logits"], inp["weights"], cfg.k, BM=128)
+        ref = O.layer_forward(inp["x"], inp["logits"], inp["weights"], cfg.k, BM=M.moe_block_m())
         check_y(y.cpu().numpy(), ref["y"], cfg.name)
 
 
@@ -182,5 +182,5 @@ def test_guard_canaries_around_outputs():
     torch.cuda.synchronize()
     assert (ybuf[:G_] == 12345.0).all() and (ybuf[G_ + n:] == 12345.0).all()
     assert (wsbuf[:256] == 0x5A).all() and (wsbuf[256 + wsn:] == 0x5A).all()
-    ref = O.layer_forward(inp["x"], inp["logits"], inp["weights"], cfg.k, BM=128)
+    ref = O.layer_forward(inp["x"], inp["logits"], inp["weights"], cfg.k, BM=M.moe_block_m())
     check_y(y.cpu().numpy(), ref["y"], "canary y")
