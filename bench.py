@@ -38,18 +38,27 @@ def expert_bytes(d, f):
     return 3 * d * f // 2 + 3 * d * f // 64 * 4
 
 
-def file_hash(path):
-    return hashlib.sha256(open(path, "rb").read()).hexdigest()[:16]
+# sources the grouped GEMM kernels are compiled from
+GEMM_SOURCES = [os.path.join("bit_quantized_grouped_router_amd", "csrc", n)
+                for n in ("moe_ffn.hip", "moe_device.h", "moe_launch.h")]
 
 
-def traffic_from_profile(kernel_src, launches_key):
-    """HBM bytes per launch measured by rocprofv3 counters, if taken on this kernel source."""
+def sources_hash(paths):
+    h = hashlib.sha256()
+    for p in paths:
+        h.update(open(os.path.join(ROOT, p), "rb").read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from_profile(sources, launches_key):
+    """HBM bytes per launch from rocprofv3 FETCH_SIZE / WRITE_SIZE counters (scaled by a
+    plain copy of known size), if they were taken on these kernel sources; else None."""
     p = os.path.join(ROOT, "profiles", "traffic.json")
     if not os.path.exists(p):
         return None
     try:
         rec = json.load(open(p)).get(launches_key)
-        if rec and rec.get("source_sha") == file_hash(kernel_src):
+        if rec and rec.get("source_sha") == sources_hash(sources):
             return rec["bytes_per_launch"]
     except Exception:
         return None
@@ -64,7 +73,7 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=512)
+    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -148,17 +157,17 @@ def main():
     for it in range(n_iter + 2):
         ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
         ev[0].record(stream)
-        M.moe_route(logits, k, ids, wts)
+        M.moe_route(logits, k, ids, wts, stream=stream)
         ev[1].record(stream)
-        M.moe_permute(dm, ids, out=perm)
+        M.moe_permute(dm, ids, out=perm, stream=stream)
         ev[2].record(stream)
         M.moe_expert_gate_up_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
-                                perm["num_tiles"], h=h)
+                                perm["num_tiles"], h=h, stream=stream)
         ev[3].record(stream)
         M.moe_expert_down_w4(dm, h, w, perm["tile_map"], perm["num_tiles"], o_routed=o_r,
-                             o_shared=o_sh)
+                             o_shared=o_sh, stream=stream)
         ev[4].record(stream)
-        M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk)
+        M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk, stream=stream)
         ev[5].record(stream)
         if it >= 2:
             evs.append(ev)
@@ -179,9 +188,7 @@ def main():
     roofline = {"kernel": "gate_up_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
-                "traffic": traffic_from_profile(
-                    os.path.join(ROOT, "bit_quantized_grouped_router_amd", "csrc", "moe_ffn.hip"),
-                    "gate_up_prefill_t4096_zipf"),
+                "traffic": traffic_from_profile(GEMM_SOURCES, "gate_up_prefill_t4096_zipf"),
                 "algorithmic_flop_per_launch": flop_gate_up}
 
     # ---------------------------------------------------------------- decode
@@ -286,7 +293,9 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16 MFMA, fp32 accumulate, int4-g64 weights",
+        "dtype": "bf16",
+        "precision": "bf16 MFMA operands (int4-g64 weights dequantised to bf16), fp32 "
+                     "accumulation, fp32 output",
         "data": "synthetic (seeded; random int4 codes, bf16 scales U(0.005,0.02), bias -8*scale)",
         "config": {"workload": "prefill_t4096_zipf: one MoE layer, T=4096, d=2048, f=512, "
                                "E=256, top-8 + 1 shared expert, Zipf(1.1)-skewed routing",

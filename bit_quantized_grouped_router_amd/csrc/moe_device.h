@@ -72,20 +72,15 @@ struct DqGroup {
 // OR-ing the nibble into the mantissa of 1024.0, and lets one mixed-precision
 // FMA form s*(1024 + q) + (b - 1024 s) = s*q + b. That equals fp32(s*q + b)
 // exactly when b - 1024 s and b - 64 s are exact in fp32 (then the FMA rounds
-// once, like the plain formula): both are sums of two 8-bit significands
-// whose exponents differ by at most 15, i.e. 2^-5 <~ |b|/s <~ 2^21 (or b == +0,
-// or s == 0), with s far from the fp32 range ends. Other groups take the
-// plain path (exactness decides, not speed).
+// once, like the plain formula): both are sums of two 8-bit significands, so
+// they are exact when the exponents of b and s differ by -5 .. 21. The test
+// below asks for that, with both exponents away from the fp32 range ends
+// (s exponent 20 .. 230, b exponent <= 230; b is then a nonzero normal
+// number). Every other group, zeros and non-finite values included, takes the
+// plain path, which is exact for all inputs.
 __device__ __forceinline__ bool dq_fast_ok(uint32_t sb) {
-  const uint32_t sbits = sb << 16, bbits = sb & 0xFFFF0000u;
-  const int es = (int)((sbits >> 23) & 0xFFu), eb = (int)((bbits >> 23) & 0xFFu);
-  const int diff = eb - es;
-  const bool s_zero = (sbits & 0x7FFFFFFFu) == 0u, b_zero = (bbits & 0x7FFFFFFFu) == 0u;
-  const bool s_ok = es >= 20 && es <= 230;
-  // b == -0 stays on the plain path: there s*0 + b is -0 for s <= -0, while
-  // the fast form cancels to +0
-  return bbits != 0x80000000u &&
-         (s_zero || (s_ok && (b_zero || (eb <= 230 && diff >= -5 && diff <= 21))));
+  const uint32_t es = (sb >> 7) & 0xFFu, eb = (sb >> 23) & 0xFFu;
+  return (es - 20u) <= 210u && eb <= 230u && (eb - es + 5u) <= 26u;
 }
 
 // The constants of the fast path (meaningful when dq_fast_ok holds).
@@ -108,25 +103,11 @@ __device__ __forceinline__ DqGroup dq_prepare(uint32_t sb) {
 
 typedef _Float16 f16x2_t __attribute__((ext_vector_type(2)));
 
-// Fast path of dequant8 (see dq_prepare): same result, 17 VALU operations.
-__device__ __forceinline__ uint4 dequant8_fast(uint32_t c, const DqGroup &q) {
-  const uint32_t y = c >> 8;
-  const f16x2_t h0 = __builtin_bit_cast(f16x2_t, (c & 0x000F000Fu) | 0x64006400u);  // cols 0, 4
-  const f16x2_t h1 = __builtin_bit_cast(f16x2_t, (c & 0x00F000F0u) | 0x64006400u);  // cols 1, 5
-  const f16x2_t h2 = __builtin_bit_cast(f16x2_t, (y & 0x000F000Fu) | 0x64006400u);  // cols 2, 6
-  const f16x2_t h3 = __builtin_bit_cast(f16x2_t, (y & 0x00F000F0u) | 0x64006400u);  // cols 3, 7
-  uint4 r;
-  r.x = pack_bf16x2(fmaf((float)h0[0], q.s, q.c0), fmaf((float)h1[0], q.s16, q.c1));
-  r.y = pack_bf16x2(fmaf((float)h2[0], q.s, q.c0), fmaf((float)h3[0], q.s16, q.c1));
-  r.z = pack_bf16x2(fmaf((float)h0[1], q.s, q.c0), fmaf((float)h1[1], q.s16, q.c1));
-  r.w = pack_bf16x2(fmaf((float)h2[1], q.s, q.c0), fmaf((float)h3[1], q.s16, q.c1));
-  return r;
-}
-
-// Constants of dequant8_fast_r held in registers for the whole kernel: gfx9
-// VOP3 encodings take no literal operand, so v_and_or_b32 needs its masks in
+// Constants of the fast dequantisation, held in registers: gfx9 VOP3
+// encodings take no literal operand, so v_and_or_b32 needs its masks in
 // registers. The asm makes the values opaque to the compiler, which would
-// otherwise fold them back into two VOP2 operations with literals.
+// otherwise fold them back into two VOP2 operations with literals (it is not
+// volatile, so repeated calls are merged into one).
 struct DqRegs {
   uint32_t m_lo, m_hi;  // 0x000F000F, 0x00F000F0 (scalar registers)
   uint32_t magic;       // 0x64006400: fp16 1024.0 in both halves (vector register)
@@ -134,9 +115,9 @@ struct DqRegs {
 
 __device__ __forceinline__ DqRegs dq_regs() {
   DqRegs r;
-  asm volatile("s_mov_b32 %0, 0x000f000f" : "=s"(r.m_lo));
-  asm volatile("s_mov_b32 %0, 0x00f000f0" : "=s"(r.m_hi));
-  asm volatile("v_mov_b32 %0, 0x64006400" : "=v"(r.magic));
+  asm("s_mov_b32 %0, 0x000f000f" : "=s"(r.m_lo));
+  asm("s_mov_b32 %0, 0x00f000f0" : "=s"(r.m_hi));
+  asm("v_mov_b32 %0, 0x64006400" : "=v"(r.magic));
   return r;
 }
 
@@ -147,10 +128,11 @@ __device__ __forceinline__ uint32_t and_or(uint32_t a, uint32_t m, uint32_t o) {
   return r;
 }
 
-// dequant8_fast with each fp16 operand built by one v_and_or_b32: 17 VALU
+// Fast path of dequant8 (see dq_fast_ok), bit-identical to it: each fp16
+// operand 1024 + q (or 1024 + 16q) is built by one v_and_or_b32; 17 VALU
 // operations for eight weights (one shift, four and-or, eight mixed FMAs,
-// four packing conversions). Same result as dequant8_fast.
-__device__ __forceinline__ uint4 dequant8_fast_r(uint32_t c, const DqGroup &q, const DqRegs &k) {
+// four packing conversions).
+__device__ __forceinline__ uint4 dequant8_fast(uint32_t c, const DqGroup &q, const DqRegs &k) {
   const uint32_t y = c >> 8;
   const f16x2_t h0 = __builtin_bit_cast(f16x2_t, and_or(c, k.m_lo, k.magic));  // cols 0, 4
   const f16x2_t h1 = __builtin_bit_cast(f16x2_t, and_or(c, k.m_hi, k.magic));  // cols 1, 5
@@ -175,10 +157,11 @@ __device__ __forceinline__ float silu_mul_fast(float g, float u) {
 __device__ __forceinline__ void dequant32(uint4 c, uint32_t sb, uint4 out[4]) {
   const DqGroup q = dq_prepare(sb);
   if (q.fast) {
-    out[0] = dequant8_fast(c.x, q);
-    out[1] = dequant8_fast(c.y, q);
-    out[2] = dequant8_fast(c.z, q);
-    out[3] = dequant8_fast(c.w, q);
+    const DqRegs k = dq_regs();
+    out[0] = dequant8_fast(c.x, q, k);
+    out[1] = dequant8_fast(c.y, q, k);
+    out[2] = dequant8_fast(c.z, q, k);
+    out[3] = dequant8_fast(c.w, q, k);
   } else {
     const float s = bf16_to_f32(sb & 0xFFFFu), b = bf16_to_f32(sb >> 16);
     out[0] = dequant8(c.x, s, b);

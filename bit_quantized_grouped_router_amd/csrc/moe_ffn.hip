@@ -28,9 +28,9 @@
 //     specialised on it and carries no per-step test;
 //   - the grid is sized from the block map's capacity (a host-side bound);
 //     workgroups past the device-side tile count exit at once, so no host
-//     synchronisation is needed; work items are spread evenly over the 8
-//     XCDs, neighbouring items (the N blocks of one tile, the tiles of one
-//     expert) on the same XCD so they share its L2.
+//     synchronisation is needed; tiles are taken in the block map's schedule
+//     order (tallest first) and dealt round-robin to the 8 XCDs, the N
+//     blocks of one tile on the same XCD so they share its L2.
 #include <type_traits>
 
 #include "moe_launch.h"
@@ -49,18 +49,20 @@ static_assert(kDma == 4, "the K loop is written for four DMA chunks per thread")
 
 enum { kGateUp = 0, kDown = 1 };
 
-// Workgroups are dispatched round-robin over the 8 XCDs (workgroup b runs on
-// XCD b % 8). Of the `active` work items (known only on the device), XCD x
-// takes the contiguous range [x*per, (x+1)*per), per = ceil(active / 8): the
-// work is spread evenly over the XCDs and neighbouring items (the N blocks
-// of one tile, the tiles of one expert) share an L2. Returns -1 for a
-// workgroup with no work. Needs gridDim.x >= 8 * per (true for a grid of at
-// least `active` workgroups, rounded up to a multiple of 8).
-__device__ __forceinline__ int xcd_remap(int bid, int active) {
-  const int per = (active + kXcds - 1) / kXcds;
-  const int slot = bid / kXcds;
-  const int logical = (bid % kXcds) * per + slot;
-  return (slot < per && logical < active) ? logical : -1;
+// Work item of workgroup bid. Workgroups are dispatched in id order,
+// round-robin over the 8 XCDs (workgroup b runs on XCD b % 8). XCD x takes
+// the tiles at schedule positions x, x + 8, x + 16, ... (the block map's
+// schedule lists the tallest tiles first), each with its nblk N blocks in
+// consecutive slots: the long work items start first on every XCD, the short
+// ones fill the tail, and the N blocks of one tile share that XCD's L2.
+// Returns false for a workgroup with no work. Needs gridDim.x >= 8 * nblk *
+// ceil(ntiles / 8).
+__device__ __forceinline__ bool sched_item(int bid, int ntiles, int nblk, int &pos, int &nb) {
+  const int x = bid % kXcds, slot = bid / kXcds;
+  const int rank = slot / nblk;
+  pos = x + kXcds * rank;
+  nb = slot - rank * nblk;
+  return pos < ntiles;
 }
 
 // s_waitcnt with only the vector-memory counter limited (expcnt and lgkmcnt
@@ -70,6 +72,17 @@ __device__ __forceinline__ int xcd_remap(int bid, int active) {
 
 typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
+
+// Activations of K step src into ring stage `stage`: this lane's four 16-byte
+// chunks (see the kernel for the lane -> row/chunk assignment).
+__device__ __forceinline__ void dma_stage(const uint16_t *act, const uint32_t (&a_off)[kDma],
+                                          uint8_t *lds, uint32_t a_lds, int src, int stage) {
+  const uint16_t *a = act + (size_t)src * kKT;
+  uint8_t *s = lds + stage * kStageBytes + a_lds;
+#pragma unroll
+  for (int i = 0; i < kDma; ++i)
+    __builtin_amdgcn_global_load_lds(a + a_off[i], (lds_void *)(s + i * 4096), 16, 0, 0);
+}
 
 // Per-workgroup state of one tile, set up once before the K loop.
 struct TileSetup {
@@ -96,7 +109,8 @@ struct TileSetup {
 // stage kt-1, code loads for step kt+2, then the four K slices.
 template <bool FULL, bool FAST>
 __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
-                                            f32x16_t (&acc)[kRB][2]) {
+                                            f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
+                                            const u32x4_t (&cr1)[2]) {
   const int lane = threadIdx.x & 63;
   const int klast = st.ksteps - 1;
   const DqRegs dk = dq_regs();
@@ -104,7 +118,8 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   // unrolled by three so every slot index is a compile-time constant. Loads
   // are unconditional: past the last step they re-read the last step, and the
   // DMA still targets the stage of step kt-1, which no one reads any more.
-  u32x4_t cr[3][2];
+  // Steps 0 and 1 (codes and activation stages) were issued by the caller.
+  u32x4_t cr[3][2] = {{cr0[0], cr0[1]}, {cr1[0], cr1[1]}, {}};
   // LDS byte address of this lane's A fragment for K slice 0 and row block 0:
   // slice ks xors its chunk index, row block rb adds rb * 4096 (the swizzle
   // depends on row % 16 only)
@@ -160,8 +175,8 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
       const uint32_t w0_ = cr[slot_][0][ks], w1_ = cr[slot_][1][ks];                         \
       uint4 d0_, d1_;                                                                        \
       if (FAST) {                                                                            \
-        d0_ = dequant8_fast_r(w0_, q0_, dk);                                                 \
-        d1_ = dequant8_fast_r(w1_, q1_, dk);                                                 \
+        d0_ = dequant8_fast(w0_, q0_, dk);                                                 \
+        d1_ = dequant8_fast(w1_, q1_, dk);                                                 \
       } else {                                                                               \
         d0_ = dequant8(w0_, ps0_, pb0_);                                                     \
         d1_ = dequant8(w1_, ps1_, pb1_);                                                     \
@@ -178,16 +193,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
     }                                                                                        \
   }
 
-  // prologue: stages 0 and 1 and the codes of steps 0 and 1 in flight, the
-  // scales of step 0 in registers
-  // (issued in the same order as inside the loop, step by step, so that the
-  // compiler's wait counts entering the loop agree with those around it)
-  MOE_DMA(0, 0);
-  MOE_LOAD_B(0, 0);
-  asm volatile("" ::: "memory");
-  MOE_DMA(min(1, klast), 1);
-  MOE_LOAD_B(min(1, klast), 1);
-  asm volatile("" ::: "memory");
+  // the scales of step 0 in registers
   sb0 = st.sbl[st.lr0];
   sb1 = st.sbl[st.lr0 + 32];
   // whole triples of steps in the loop (every path through its body is the
@@ -224,10 +230,11 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
   const int ncols = KIND == kGateUp ? f : d;          // gate/up: units; down: output columns
   const int wg_cols = KIND == kGateUp ? kWgCols / 2 : kWgCols;
   const int nblk = (ncols + wg_cols - 1) / wg_cols;
-  const int logical = xcd_remap(blockIdx.x, *num_tiles_p * nblk);
-  if (logical < 0) return;
-  const int tile = logical / nblk;
-  const int n0 = (logical % nblk) * wg_cols;
+  int pos, nb;
+  const int ntiles = *num_tiles_p;
+  if (!sched_item(blockIdx.x, ntiles, nblk, pos, nb)) return;
+  const int tile = min(max(tile_map[4 * (size_t)pos + 3], 0), ntiles - 1);  // in range for any map
+  const int n0 = nb * wg_cols;
   const int4 tm = *(const int4 *)(tile_map + 4 * (size_t)tile);
   const int g = tm.x, row_begin = tm.y, row_end = tm.z;
   const bool shared = g >= E;
@@ -240,28 +247,25 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
   TileSetup st;
   st.act = act;
   st.ksteps = K / kKT;
-  // ---- activation rows. DMA instruction i of wavefront w fills tile rows
+  const int klast = st.ksteps - 1;
+  // ---- prologue. The loads go out in dependency order so that their
+  // latencies overlap: token indices (they gate the activation DMA), codes of
+  // steps 0 and 1 and the tile's scales (they need only the tile), then the
+  // DMA of stages 0 and 1; the scale table is written while the DMA is in
+  // flight.
+  //
+  // Activation rows: DMA instruction i of wavefront w fills tile rows
   // 32 i + 8 w .. +7 (1 KB, 16 bytes per lane in lane order); lane l lands in
   // row r = 32 i + 8 w + l / 8 at 16-byte slot l % 8, which holds logical
   // chunk (l % 8) ^ (r % 8) ^ ((r / 8) % 2) of the row (the swizzle). Rows
   // past the tile's end re-read its last row (their results are never
   // stored), so every load is unconditional.
   st.a_lds = (uint32_t)wave * 1024u;
-  {
-    const int j = (lane & 7) ^ (lane >> 3) ^ (wave & 1);
+  int tok[kDma];
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      const int p = min(row_begin + 32 * i + 8 * wave + (lane >> 3), row_end - 1);
-      uint32_t row;
-      if (KIND == kGateUp) {
-        int tok = shared ? p - TK : sorted_token[p];
-        tok = tok < 0 ? 0 : (tok >= T ? T - 1 : tok);  // in range even for malformed routing
-        row = (uint32_t)tok;
-      } else {
-        row = (uint32_t)p;
-      }
-      st.a_off[i] = row * (uint32_t)K + (uint32_t)j * 8u;
-    }
+  for (int i = 0; i < kDma; ++i) {
+    const int p = min(row_begin + 32 * i + 8 * wave + (lane >> 3), row_end - 1);
+    tok[i] = KIND == kGateUp ? (shared ? p - TK : sorted_token[p]) : p;
   }
   // ---- this wavefront's two 32-row blocks of weight rows
   bool wave_on;  // wave-uniform: this wavefront has weight rows (both blocks: f, d % 64 == 0)
@@ -283,39 +287,76 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
                                                (short)0, nrows_w * (K / 2), 0x00020000);
   st.c_off[0] = R0 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
   st.c_off[1] = R1 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
-  // ---- the scale/bias table: lane l of wavefront w fills column 64 w + l,
-  // which is weight row R0 (l < 32) or R1 (l >= 32) of lane l % 32, for all
-  // groups; the wavefront reads back only its own columns. The same pass
-  // decides whether all of them allow the fast dequantisation.
+  u32x4_t cr0[2], cr1[2];
+#pragma unroll
+  for (int b = 0; b < 2; ++b) {
+    cr0[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(st.codes, st.c_off[b], 0, 0));
+    cr1[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                             st.codes, st.c_off[b], min(1, klast) * (kKT / 2), 0));
+  }
+  // the scale/bias table: lane l of wavefront w fills column 64 w + l, which
+  // is weight row R0 (l < 32) or R1 (l >= 32) of lane l % 32, for all groups;
+  // the wavefront reads back only its own columns. The same pass decides
+  // whether all of them allow the fast dequantisation. Groups are taken 32 at
+  // a time with all their loads issued together.
   st.sbl = sbl;
   st.lr0 = wave * 64 + (lane & 31);
+  const int ng = K / kGroup;
+  const size_t srow = (ex * (size_t)nrows_w + ((lane >> 5) ? R1 : R0)) * (size_t)ng;
+  const uint16_t *sp = W.scales + srow, *bp = W.biases + srow;
+  uint32_t *col = sbl + wave * 64 + lane;
   bool fast_ok = true;
+  const bool vec = ng % 8 == 0;  // rows start 16-byte aligned: 16-byte loads
+  uint4 sv[4], bv[4];
+  if (vec) {
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int g0 = min(8 * q, ng - 8);
+      sv[q] = *(const uint4 *)(sp + g0);
+      bv[q] = *(const uint4 *)(bp + g0);
+    }
+  }
+  // token rows -> activation offsets, then the DMA of stages 0 and 1
   {
-    const uint32_t R = (lane >> 5) ? R1 : R0;
-    const int ng = K / kGroup;
-    const size_t srow = (ex * (size_t)nrows_w + R) * (size_t)ng;
-    const uint16_t *sp = W.scales + srow, *bp = W.biases + srow;
-    uint32_t *col = sbl + wave * 64 + lane;
-    if (ng % 8 == 0) {
-      // 16-byte loads: each row starts 16-byte aligned (ng * 2 bytes per row)
-      for (int g0 = 0; g0 < ng; g0 += 8) {
-        const uint4 sv = *(const uint4 *)(sp + g0), bv = *(const uint4 *)(bp + g0);
-        const uint32_t su[4] = {sv.x, sv.y, sv.z, sv.w}, bu[4] = {bv.x, bv.y, bv.z, bv.w};
+    const uint32_t j = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
+#pragma unroll
+    for (int i = 0; i < kDma; ++i) {
+      const int t = KIND == kGateUp ? (tok[i] < 0 ? 0 : (tok[i] >= T ? T - 1 : tok[i])) : tok[i];
+      st.a_off[i] = (uint32_t)t * (uint32_t)K + j * 8u;  // token clamped: in range for any routing
+    }
+  }
+  dma_stage(act, st.a_off, smem, st.a_lds, 0, 0);
+  dma_stage(act, st.a_off, smem, st.a_lds, min(1, klast), 1);
+  if (vec) {
+    for (int g0 = 0; g0 < ng; g0 += 32) {
+      if (g0 > 0) {
 #pragma unroll
         for (int q = 0; q < 4; ++q) {
-          const uint32_t w0 = (su[q] & 0xFFFFu) | (bu[q] << 16);
-          const uint32_t w1 = (su[q] >> 16) | (bu[q] & 0xFFFF0000u);
-          col[(g0 + 2 * q) * kWgCols] = w0;
-          col[(g0 + 2 * q + 1) * kWgCols] = w1;
-          fast_ok &= dq_fast_ok(w0) & dq_fast_ok(w1);
+          const int g1 = min(g0 + 8 * q, ng - 8);
+          sv[q] = *(const uint4 *)(sp + g1);
+          bv[q] = *(const uint4 *)(bp + g1);
         }
       }
-    } else {
-      for (int g0 = 0; g0 < ng; ++g0) {
-        const uint32_t w0 = (uint32_t)sp[g0] | ((uint32_t)bp[g0] << 16);
-        col[g0 * kWgCols] = w0;
-        fast_ok &= dq_fast_ok(w0);
+#pragma unroll
+      for (int q = 0; q < 4; ++q) {
+        if (g0 + 8 * q >= ng) break;
+        const uint32_t su[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
+        const uint32_t bu[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const uint32_t w0 = (su[e] & 0xFFFFu) | (bu[e] << 16);
+          const uint32_t w1 = (su[e] >> 16) | (bu[e] & 0xFFFF0000u);
+          col[(g0 + 8 * q + 2 * e) * kWgCols] = w0;
+          col[(g0 + 8 * q + 2 * e + 1) * kWgCols] = w1;
+          fast_ok &= (int)dq_fast_ok(w0) & (int)dq_fast_ok(w1);
+        }
       }
+    }
+  } else {
+    for (int g0 = 0; g0 < ng; ++g0) {
+      const uint32_t w0 = (uint32_t)sp[g0] | ((uint32_t)bp[g0] << 16);
+      col[g0 * kWgCols] = w0;
+      fast_ok &= dq_fast_ok(w0);
     }
   }
   const bool fast = __builtin_amdgcn_ballot_w64(!fast_ok) == 0;  // wave-uniform
@@ -325,47 +366,102 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
   f32x16_t acc[kRB][2];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
+  // stage 0 has landed (only the four chunks of stage 1 may still be in
+  // flight); the loop's first wait then holds at once
+  MOE_WAIT_VMCNT(kDma);
   if (st.nrb == kRB) {
     if (fast)
-      gemm_k_loop<true, true>(st, smem, acc);
+      gemm_k_loop<true, true>(st, smem, acc, cr0, cr1);
     else
-      gemm_k_loop<true, false>(st, smem, acc);
+      gemm_k_loop<true, false>(st, smem, acc, cr0, cr1);
   } else {
     if (fast)
-      gemm_k_loop<false, true>(st, smem, acc);
+      gemm_k_loop<false, true>(st, smem, acc, cr0, cr1);
     else
-      gemm_k_loop<false, false>(st, smem, acc);
+      gemm_k_loop<false, false>(st, smem, acc, cr0, cr1);
   }
 
-  // epilogue; C layout of the 32x32 MFMA: lane l holds column l%32, register
-  // r holds row 8*(r/4) + 4*(l/32) + r%4
+  // ---- epilogue. Every wavefront is past its last LDS read of the ring
+  // before any wavefront reuses the LDS.
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   if (!wave_on) return;
+  // C layout of the 32x32 MFMA: lane l holds column l%32, register r holds
+  // row 8*(r/4) + 4*(l/32) + r%4
+  const int c = lane & 31, hh = lane >> 5;
+  if (KIND == kDown && shared) {
+    // fp32 rows of the shared expert: 128 contiguous bytes per half-wavefront
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      if (rb >= st.nrb) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = row_begin + rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        if (p >= row_end) continue;
+        out_f32[(size_t)(p - TK) * d + wrow0] = acc[rb][0][r];
+        out_f32[(size_t)(p - TK) * d + wrow1] = acc[rb][1][r];
+      }
+    }
+    return;
+  }
+  // bf16 outputs go through this wavefront's LDS region as [row][col] tiles
+  // and leave as 16-byte row chunks. gate/up: 32 columns (64 bytes) per row,
+  // physical row r ^ (2 * ((r / 4) % 2)); down: 64 columns (128 bytes) per
+  // row, 16-byte chunk j stored at j ^ (4 * ((r / 4) % 2)). Either way the
+  // two halves of the wavefront (rows r and r + 4) write disjoint banks.
+  uint8_t *ep = smem + wave * (KIND == kGateUp ? 8192 : 16384);
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     if (rb >= st.nrb) continue;
 #pragma unroll
-    for (int r = 0; r < 16; ++r) {
-      const int p = row_begin + rb * 32 + (r >> 2) * 8 + (lane >> 5) * 4 + (r & 3);
-      if (p >= row_end) continue;
+    for (int r = 0; r < 16; r += 2) {
+      const int row = rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);  // even; row + 1 is r + 1's
       if (KIND == kGateUp) {
-        out_bf16[(size_t)p * f + wrow0] = to_bf16(silu_mul_fast(acc[rb][0][r], acc[rb][1][r]));
-      } else if (shared) {
-        out_f32[(size_t)(p - TK) * d + wrow0] = acc[rb][0][r];
-        out_f32[(size_t)(p - TK) * d + wrow1] = acc[rb][1][r];
+        const uint32_t pk = pack_bf16x2(silu_mul_fast(acc[rb][0][r], acc[rb][1][r]),
+                                        silu_mul_fast(acc[rb][0][r + 1], acc[rb][1][r + 1]));
+        const int pr = row ^ (((row >> 2) & 1) << 1);
+        *(uint16_t *)(ep + pr * 64 + c * 2) = (uint16_t)pk;
+        *(uint16_t *)(ep + (pr + 1) * 64 + c * 2) = (uint16_t)(pk >> 16);
       } else {
-        out_bf16[(size_t)p * d + wrow0] = to_bf16(acc[rb][0][r]);
-        out_bf16[(size_t)p * d + wrow1] = to_bf16(acc[rb][1][r]);
+        const int sw = ((row >> 2) & 1) * 4;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t pk = pack_bf16x2(acc[rb][b][r], acc[rb][b][r + 1]);
+          const int off = ((((b * 32 + c) >> 3) ^ sw) << 4) + (c & 7) * 2;
+          *(uint16_t *)(ep + row * 128 + off) = (uint16_t)pk;
+          *(uint16_t *)(ep + (row + 1) * 128 + off) = (uint16_t)(pk >> 16);
+        }
       }
+    }
+  }
+  if (KIND == kGateUp) {
+    const int unit = n0 + wave * 32;
+    for (int it = 0; it < st.nrb * 2; ++it) {
+      const int r = it * 16 + (lane >> 2), j = lane & 3;
+      const int pr = r ^ (((r >> 2) & 1) << 1);
+      const uint4 v = *(const uint4 *)(ep + pr * 64 + j * 16);
+      const int p = row_begin + r;
+      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * f + unit + j * 8) = v;
+    }
+  } else {
+    const int col0 = n0 + wave * 64;
+    for (int it = 0; it < st.nrb * 4; ++it) {
+      const int r = it * 8 + (lane >> 3), j = lane & 7;
+      const uint4 v = *(const uint4 *)(ep + r * 128 + ((j ^ (((r >> 2) & 1) * 4)) << 4));
+      const int p = row_begin + r;
+      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * d + col0 + j * 8) = v;
     }
   }
 }
 
-static int round_up8(long long n) { return (int)((n + kXcds - 1) / kXcds * kXcds); }
+static long long round_up8(long long n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 // LDS of one GEMM workgroup for input width K: the activation ring and the
 // scale/bias table (K/64 groups x 256 weight rows x 4 bytes).
 static size_t gemm_lds_bytes(int K) {
-  return (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
+  const size_t loop = (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
+  const size_t epilogue = 4 * 16384;  // four wavefronts x 128 rows x 128 bytes (down)
+  return loop > epilogue ? loop : epilogue;
 }
 
 // More than 64 KB of dynamic LDS needs a per-kernel opt-in (once per process).
@@ -387,7 +483,7 @@ hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
                           const int32_t *num_tiles, uint16_t *h, hipStream_t s) {
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.f + kWgCols / 2 - 1) / (kWgCols / 2);
-  const int grid = round_up8((long long)tile_capacity(dm) * nblk);
+  const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
   grouped_gemm_w4_kernel<kGateUp><<<grid, 256, gemm_lds_bytes(dm.d), s>>>(
       x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
       dm.k);
@@ -399,7 +495,7 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const Weights &w,
                        float *o_shared, hipStream_t s) {
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.d + kWgCols - 1) / kWgCols;
-  const int grid = round_up8((long long)tile_capacity(dm) * nblk);
+  const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
   grouped_gemm_w4_kernel<kDown><<<grid, 256, gemm_lds_bytes(dm.f), s>>>(
       h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
       dm.k);

@@ -7,7 +7,10 @@
 //   perm_hist    per block of 256 tokens, a per-expert count (LDS atomics);
 //   perm_scan    one workgroup: per-expert running prefix over the blocks,
 //                exclusive scan over experts (offsets), tiles per group and
-//                their exclusive scan, then the tile map;
+//                their exclusive scan, then the tile map, and the order the
+//                grouped GEMMs take the tiles in (fourth column: tallest
+//                first, so the longest work items start first and the short
+//                ones fill the tail of the launch);
 //   perm_scatter per block, the rank of each assignment among the block's
 //                assignments to the same expert, from a token bitmask per
 //                expert (popcount of the bits below the token), so the row
@@ -62,6 +65,15 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *wave_tot) {
   return v + add;
 }
 
+// Tiles are full (kBlockM rows) except the last of each group (c % kBlockM
+// rows). The schedule (fourth column of the tile map: row i names the i-th
+// tile to run) lists every full tile in tile order, then the partial tiles
+// by decreasing height, equal heights in tile order. Partial tiles are
+// ranked with one LDS bitmask of groups per height, so the order is exact
+// and independent of the order atomics happen in.
+constexpr int kMaxGroups = kMaxExperts + 1;
+constexpr int kGroupWords = (kMaxGroups + 31) / 32;
+
 __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ block_counts,
                                                          int nblocks, int T, int E, int k,
                                                          int32_t *__restrict__ counts,
@@ -69,8 +81,11 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
                                                          int32_t *__restrict__ tile_map,
                                                          int32_t *__restrict__ num_tiles) {
   __shared__ int wave_tot[16];
-  __shared__ int s_routed_tiles;
+  __shared__ int s_routed_tiles, s_routed_full;
+  __shared__ uint32_t hmask[kBlockM][kGroupWords];  // groups whose partial tile has height r
+  __shared__ int hstart[kBlockM];                   // schedule position of height r's first tile
   const int e = threadIdx.x;
+  for (int i = e; i < kBlockM * kGroupWords; i += blockDim.x) (&hmask[0][0])[i] = 0u;
   // per-expert running prefix over token blocks, in place
   int c = 0;
   if (e < E) {
@@ -82,22 +97,30 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
     }
   }
   const int nt = (c + kBlockM - 1) / kBlockM;
+  const int nf = c / kBlockM;  // full tiles
   const int c_incl = block_inclusive_scan(c, wave_tot);
   const int nt_incl = block_inclusive_scan(nt, wave_tot);
+  const int nf_incl = block_inclusive_scan(nf, wave_tot);
   const int off = c_incl - c;
   const int tbase = nt_incl - nt;
+  const int fbase = nf_incl - nf;
   if (e < E) {
     counts[e] = c;
     offsets[e] = off;
     for (int i = 0; i < nt; ++i) {
       const int rb = off + i * kBlockM;
       const int re = min(rb + kBlockM, off + c);
-      *(int4 *)(tile_map + 4 * (size_t)(tbase + i)) = make_int4(e, rb, re, 0);
+      int32_t *row = tile_map + 4 * (size_t)(tbase + i);
+      row[0] = e;
+      row[1] = rb;
+      row[2] = re;
     }
+    if (c % kBlockM) atomicOr(&hmask[c % kBlockM][e >> 5], 1u << (e & 31));
   }
   if (e == blockDim.x - 1) {
     offsets[E] = c_incl;  // == T*k
     s_routed_tiles = nt_incl;
+    s_routed_full = nf_incl;
   }
   __syncthreads();
   // the shared group E: rows T*k .. T*k+T-1
@@ -107,9 +130,45 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   for (int i = e; i < ns; i += blockDim.x) {
     const int rb = sh0 + i * kBlockM;
     const int re = min(rb + kBlockM, sh0 + T);
-    *(int4 *)(tile_map + 4 * (size_t)(rbase + i)) = make_int4(E, rb, re, 0);
+    int32_t *row = tile_map + 4 * (size_t)(rbase + i);
+    row[0] = E;
+    row[1] = rb;
+    row[2] = re;
   }
-  if (e == 0) *num_tiles = rbase + ns;
+  if (e == 0) {
+    *num_tiles = rbase + ns;
+    if (T % kBlockM) atomicOr(&hmask[T % kBlockM][E >> 5], 1u << (E & 31));
+  }
+  __syncthreads();
+  // tiles per height, then the first schedule position of each height
+  // (heights kBlockM-1 .. 1 after all full tiles)
+  const int nfull = s_routed_full + T / kBlockM;
+  int hc = 0;
+  const int hgt = kBlockM - 1 - e;  // thread e counts height kBlockM-1-e (e < kBlockM-1)
+  if (e < kBlockM - 1)
+    for (int w = 0; w < kGroupWords; ++w) hc += __popc(hmask[hgt][w]);
+  const int hc_incl = block_inclusive_scan(e < kBlockM - 1 ? hc : 0, wave_tot);
+  if (e < kBlockM - 1) hstart[hgt] = nfull + hc_incl - hc;
+  __syncthreads();
+  // schedule entries: full routed tiles, full shared tiles, partial tiles
+  if (e < E) {
+    for (int i = 0; i < nf; ++i) tile_map[4 * (size_t)(fbase + i) + 3] = tbase + i;
+    const int r = c % kBlockM;
+    if (r) {
+      int rank = __popc(hmask[r][e >> 5] & ((1u << (e & 31)) - 1u));
+      for (int w = 0; w < (e >> 5); ++w) rank += __popc(hmask[r][w]);
+      tile_map[4 * (size_t)(hstart[r] + rank) + 3] = tbase + nf;
+    }
+  }
+  for (int i = e; i < T / kBlockM; i += blockDim.x)
+    tile_map[4 * (size_t)(s_routed_full + i) + 3] = rbase + i;
+  if (e == 0 && T % kBlockM) {
+    const int r = T % kBlockM;
+    int rank = 0;
+    for (int w = 0; w <= (E >> 5); ++w)
+      rank += __popc(w < (E >> 5) ? hmask[r][w] : (hmask[r][w] & ((1u << (E & 31)) - 1u)));
+    tile_map[4 * (size_t)(hstart[r] + rank) + 3] = rbase + ns - 1;
+  }
 }
 
 __global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(

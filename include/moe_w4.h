@@ -123,13 +123,17 @@ size_t moe_permute_workspace_bytes(const moe_dims *dm);
  *   offsets      int32 [E+1]          out: exclusive scan, offsets[E] = T*k
  *   sorted_token int32 [T*k]          out: token of each permuted row
  *   row_of       int32 [T*k]          out: permuted row of assignment t*k+j
- *   tile_map     int32 [cap][4]       out: {group, row_begin, row_end, 0} per
- *                                     tile, cap = moe_tile_capacity(dm);
+ *   tile_map     int32 [cap][4]       out: {group, row_begin, row_end, sched}
+ *                                     per tile, cap = moe_tile_capacity(dm);
  *                                     groups 0..E-1 in order, then the shared
  *                                     group E (rows T*k .. T*k+T-1); each group
  *                                     split into ceil(count/BM) tiles of at most
- *                                     BM = moe_block_m() rows. Entries past
- *                                     num_tiles are left untouched.
+ *                                     BM = moe_block_m() rows. sched of row i is
+ *                                     the index of the i-th tile in the order
+ *                                     the grouped GEMMs run them: tallest tile
+ *                                     first, equal heights in tile order (a
+ *                                     permutation of 0..num_tiles-1). Entries
+ *                                     past num_tiles are left untouched.
  *   num_tiles    int32 [1]            out: tiles written
  *   ws, ws_bytes                      scratch, >= moe_permute_workspace_bytes(dm)
  * Deterministic: the row order does not depend on scheduling.

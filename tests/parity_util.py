@@ -66,3 +66,11 @@ def check_bf16_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str, max_frac:
     say(f"  {what}: {frac:.2e} of elements differ, max diff {float((diff / ulp).max()):.2f} ulp")
     assert (diff <= ulp * 1.0000001 + slack).all(), f"{what}: difference above one bf16 ulp"
     assert frac <= max_frac, f"{what}: {frac:.3e} of elements differ"
+
+
+def expected_schedule(tiles) -> np.ndarray:
+    """The block map's fourth column: tile indices, tallest tile first, equal heights
+    in tile order (the order the grouped GEMMs take the tiles in)."""
+    tiles = np.asarray(tiles)
+    heights = tiles[:, 2] - tiles[:, 1]
+    return np.array(sorted(range(len(tiles)), key=lambda i: (-int(heights[i]), i)), dtype=np.int64)

@@ -14,7 +14,7 @@ import torch
 import bit_quantized_grouped_router_amd as M
 import moe_inputs as G
 from oracle import moe_oracle as O
-from parity_util import W_ABS, check_y, dev_bits, say, upload
+from parity_util import W_ABS, check_y, dev_bits, expected_schedule, say, upload
 
 pytestmark = pytest.mark.gpu
 
@@ -49,6 +49,7 @@ def _check_routing(cfg, inp, dm, logits):
     n = int(p["num_tiles"][0])
     assert n == len(tiles) <= M.moe_tile_capacity(dm)
     assert np.array_equal(p["tile_map"][:n, :3], tiles)
+    assert np.array_equal(p["tile_map"][:n, 3], expected_schedule(tiles))
     return counts
 
 
