@@ -145,7 +145,27 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
                                                  st.codes, st.c_off[1], (kt_) * (kKT / 2), 0)); \
   }
 
-  // one K step; slot_ is a literal (0..2) equal to kt_ % 3
+  // B fragments (dequantised codes) of one K slice of this lane's two weight
+  // rows; q*_ / p*_ are the group constants of the step the codes belong to
+#define MOE_DQ(w0_, w1_, q0_, q1_, sb0_, sb1_, out0_, out1_)                                   \
+  {                                                                                          \
+    uint4 d0_, d1_;                                                                          \
+    if (FAST) {                                                                              \
+      d0_ = dequant8_fast(w0_, q0_, dk);                                                     \
+      d1_ = dequant8_fast(w1_, q1_, dk);                                                     \
+    } else {                                                                                 \
+      d0_ = dequant8(w0_, bf16_to_f32((sb0_) & 0xFFFFu), bf16_to_f32((sb0_) >> 16));         \
+      d1_ = dequant8(w1_, bf16_to_f32((sb1_) & 0xFFFFu), bf16_to_f32((sb1_) >> 16));         \
+    }                                                                                        \
+    out0_ = __builtin_bit_cast(bf16x8_t, d0_);                                               \
+    out1_ = __builtin_bit_cast(bf16x8_t, d1_);                                               \
+  }
+
+  // one K step; slot_ is a literal (0..2) equal to kt_ % 3. The B fragments
+  // are rebuilt one K slice ahead: while the MFMAs of slice ks run, the VALU
+  // rebuilds slice ks + 1 (after slice 3: slice 0 of the next step, from the
+  // codes and scales already in registers), so the dequantisation and the
+  // matrix cores work on independent data.
 #define MOE_STEP(kt_, slot_)                                                                 \
   {                                                                                          \
     const int ktv_ = (kt_);                                                                  \
@@ -162,40 +182,38 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
       sb1 = st.sbl[kn_ + 32];                                                                \
     }                                                                                        \
     const uint8_t *abuf_ = lds + (ktv_ % kStages) * kStageBytes;                             \
-    DqGroup q0_, q1_;                                                                        \
-    float ps0_ = 0.f, pb0_ = 0.f, ps1_ = 0.f, pb1_ = 0.f;                                    \
-    if (FAST) {                                                                              \
-      q0_ = dq_consts(s0_);                                                                  \
-      q1_ = dq_consts(s1_);                                                                  \
-    } else {                                                                                 \
-      ps0_ = bf16_to_f32(s0_ & 0xFFFFu), pb0_ = bf16_to_f32(s0_ >> 16);                      \
-      ps1_ = bf16_to_f32(s1_ & 0xFFFFu), pb1_ = bf16_to_f32(s1_ >> 16);                      \
-    }                                                                                        \
+    const DqGroup q0_ = dq_consts(s0_), q1_ = dq_consts(s1_);                                \
     _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                       \
-      const uint32_t w0_ = cr[slot_][0][ks], w1_ = cr[slot_][1][ks];                         \
-      uint4 d0_, d1_;                                                                        \
-      if (FAST) {                                                                            \
-        d0_ = dequant8_fast(w0_, q0_, dk);                                                 \
-        d1_ = dequant8_fast(w1_, q1_, dk);                                                 \
-      } else {                                                                               \
-        d0_ = dequant8(w0_, ps0_, pb0_);                                                     \
-        d1_ = dequant8(w1_, ps1_, pb1_);                                                     \
-      }                                                                                      \
-      const bf16x8_t b0_ = __builtin_bit_cast(bf16x8_t, d0_);                                \
-      const bf16x8_t b1_ = __builtin_bit_cast(bf16x8_t, d1_);                                \
       const uint8_t *aks_ = abuf_ + lrow + (((lh + ks) ^ lx) << 4);                          \
+      bf16x8_t a_[kRB];                                                                      \
+      _Pragma("unroll") for (int rb = 0; rb < kRB; ++rb)                                     \
+        a_[rb] = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks_ + rb * 4096));           \
+      bf16x8_t n0_, n1_;                                                                     \
+      if (ks < 3) {                                                                          \
+        MOE_DQ(cr[slot_][0][ks + 1], cr[slot_][1][ks + 1], q0_, q1_, s0_, s1_, n0_, n1_);    \
+      } else {                                                                               \
+        const DqGroup r0_ = dq_consts(sb0), r1_ = dq_consts(sb1);                            \
+        MOE_DQ(cr[((slot_) + 1) % 3][0][0], cr[((slot_) + 1) % 3][1][0], r0_, r1_, sb0, sb1, \
+               n0_, n1_);                                                                    \
+      }                                                                                      \
       _Pragma("unroll") for (int rb = 0; rb < kRB; ++rb) {                                   \
         if (!FULL && rb >= st.nrb) continue;                                                 \
-        const bf16x8_t a_ = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks_ + rb * 4096)); \
-        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, b0_, acc[rb][0], 0, 0, 0);  \
-        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_, b1_, acc[rb][1], 0, 0, 0);  \
+        acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[rb], bq0, acc[rb][0], 0, 0, 0); \
+        acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[rb], bq1, acc[rb][1], 0, 0, 0); \
       }                                                                                      \
+      bq0 = n0_;                                                                             \
+      bq1 = n1_;                                                                             \
     }                                                                                        \
   }
 
-  // the scales of step 0 in registers
+  // the scales of step 0, slice 0 of step 0 rebuilt
   sb0 = st.sbl[st.lr0];
   sb1 = st.sbl[st.lr0 + 32];
+  bf16x8_t bq0, bq1;
+  {
+    const DqGroup r0 = dq_consts(sb0), r1 = dq_consts(sb1);
+    MOE_DQ(cr[0][0][0], cr[0][1][0], r0, r1, sb0, sb1, bq0, bq1);
+  }
   // whole triples of steps in the loop (every path through its body is the
   // same, so the memory wait counters carried around the loop are exact),
   // then the one or two remaining steps
@@ -210,6 +228,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   // no DMA may still be writing LDS when the workgroup ends
   MOE_WAIT_VMCNT(0);
 #undef MOE_STEP
+#undef MOE_DQ
 #undef MOE_DMA
 #undef MOE_LOAD_B
 }
