@@ -45,7 +45,9 @@ constexpr int kStageBytes = kBlockM * 128;   // one K step of the tile's rows, b
 constexpr int kDma = kBlockM * 8 / 256;      // 16-byte DMA chunks per thread per K step
 constexpr int kXcds = 8;
 
-static_assert(kDma == 4, "the K loop is written for four DMA chunks per thread");
+// workgroups per CU the register budget is sized for (128-row tiles leave
+// room for two; 256-row tiles need all 512 registers of a lane)
+constexpr int kOcc = kBlockM <= 128 ? 2 : 1;
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -128,15 +130,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   uint32_t sb0, sb1;
 
   // activations of K step src_ into ring stage stage_
-#define MOE_DMA(src_, stage_)                                                                \
-  {                                                                                          \
-    const uint16_t *a_ = st.act + (size_t)(src_) * kKT;                                      \
-    uint8_t *s_ = lds + (stage_) * kStageBytes + st.a_lds;                                   \
-    __builtin_amdgcn_global_load_lds(a_ + st.a_off[0], (lds_void *)(s_ + 0 * 4096), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(a_ + st.a_off[1], (lds_void *)(s_ + 1 * 4096), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(a_ + st.a_off[2], (lds_void *)(s_ + 2 * 4096), 16, 0, 0); \
-    __builtin_amdgcn_global_load_lds(a_ + st.a_off[3], (lds_void *)(s_ + 3 * 4096), 16, 0, 0); \
-  }
+#define MOE_DMA(src_, stage_) dma_stage(st.act, st.a_off, lds, st.a_lds, (src_), (stage_))
 #define MOE_LOAD_B(kt_, slot_)                                                              \
   {                                                                                         \
     cr[slot_][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(       \
@@ -234,7 +228,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
 }
 
 template <int KIND>
-__global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
+__global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
     const uint16_t *__restrict__ act, W4 wr, W4 ws, const int32_t *__restrict__ sorted_token,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ num_tiles_p,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32, int T, int d, int f, int E,
@@ -428,7 +422,7 @@ __global__ __launch_bounds__(256, 2) void grouped_gemm_w4_kernel(
   // physical row r ^ (2 * ((r / 4) % 2)); down: 64 columns (128 bytes) per
   // row, 16-byte chunk j stored at j ^ (4 * ((r / 4) % 2)). Either way the
   // two halves of the wavefront (rows r and r + 4) write disjoint banks.
-  uint8_t *ep = smem + wave * (KIND == kGateUp ? 8192 : 16384);
+  uint8_t *ep = smem + wave * (KIND == kGateUp ? kBlockM * 64 : kBlockM * 128);
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) {
     if (rb >= st.nrb) continue;
@@ -479,7 +473,7 @@ static long long round_up8(long long n) { return (n + kXcds - 1) / kXcds * kXcds
 // scale/bias table (K/64 groups x 256 weight rows x 4 bytes).
 static size_t gemm_lds_bytes(int K) {
   const size_t loop = (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
-  const size_t epilogue = 4 * 16384;  // four wavefronts x 128 rows x 128 bytes (down)
+  const size_t epilogue = 4 * kBlockM * 128;  // four wavefronts x kBlockM rows x 128 bytes (down)
   return loop > epilogue ? loop : epilogue;
 }
 

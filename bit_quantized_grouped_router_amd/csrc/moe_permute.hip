@@ -86,14 +86,22 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   __shared__ int hstart[kBlockM];                   // schedule position of height r's first tile
   const int e = threadIdx.x;
   for (int i = e; i < kBlockM * kGroupWords; i += blockDim.x) (&hmask[0][0])[i] = 0u;
-  // per-expert running prefix over token blocks, in place
+  // per-expert running prefix over token blocks, in place; the counts of 16
+  // blocks are loaded together before any is overwritten (a load after a
+  // store to the same array would otherwise wait for a full round trip each)
   int c = 0;
   if (e < E) {
-    for (int b = 0; b < nblocks; ++b) {
-      int32_t *p = block_counts + (size_t)b * E + e;
-      const int v = *p;
-      *p = c;
-      c += v;
+    constexpr int kChunk = 16;
+    for (int b0 = 0; b0 < nblocks; b0 += kChunk) {
+      int v[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        v[i] = b0 + i < nblocks ? block_counts[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (b0 + i < nblocks) block_counts[(size_t)(b0 + i) * E + e] = c;
+        c += v[i];
+      }
     }
   }
   const int nt = (c + kBlockM - 1) / kBlockM;
