@@ -75,23 +75,27 @@ __device__ __forceinline__ bool sched_item(int bid, int ntiles, int nblk, int &p
 typedef __attribute__((address_space(3))) void lds_void;
 typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 
-// Activations of K step src into ring stage `stage`: this lane's four 16-byte
-// chunks (see the kernel for the lane -> row/chunk assignment).
-__device__ __forceinline__ void dma_stage(const uint16_t *act, const uint32_t (&a_off)[kDma],
-                                          uint8_t *lds, uint32_t a_lds, int src, int stage) {
-  const uint16_t *a = act + (size_t)src * kKT;
+// Activations of K step src into ring stage `stage`: this lane's 16-byte
+// chunks (see the kernel for the lane -> row/chunk assignment), LDS DMA
+// through a buffer resource (byte offsets: a_off, plus the step as a scalar).
+__device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t actr,
+                                          const uint32_t (&a_off)[kDma], uint8_t *lds,
+                                          uint32_t a_lds, int src, int stage) {
   uint8_t *s = lds + stage * kStageBytes + a_lds;
 #pragma unroll
   for (int i = 0; i < kDma; ++i)
-    __builtin_amdgcn_global_load_lds(a + a_off[i], (lds_void *)(s + i * 4096), 16, 0, 0);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(actr, (lds_void *)(s + i * 4096), 16, a_off[i],
+                                             src * (kKT * 2), 0, 0);
 }
 
 // Per-workgroup state of one tile, set up once before the K loop.
 struct TileSetup {
-  const uint16_t *act;    // activation matrix (x for gate/up, h for down)
-  uint32_t a_off[kDma];   // element offsets (K step 0) of this lane's DMA chunks
+  __amdgpu_buffer_rsrc_t actr;       // activation matrix (x for gate/up, h for down)
+  __amdgpu_buffer_rsrc_t actr_none;  // the same with no records: every access out of range
+  uint32_t a_off[kDma];   // byte offsets (K step 0) of this lane's DMA chunks
   uint32_t a_lds;         // LDS byte offset of this wavefront's first DMA slot in a stage
-  __amdgpu_buffer_rsrc_t codes;  // the expert's codes
+  __amdgpu_buffer_rsrc_t codes;       // the expert's codes
+  __amdgpu_buffer_rsrc_t codes_none;  // the same with no records
   uint32_t c_off[2];      // byte offsets of this lane's two weight rows (plus its half)
   const uint32_t *sbl;    // LDS table [K/64][256] of (scale | bias << 16) per weight row
   int lr0;                // this lane's table column for block 0 (block 1 adds 32)
@@ -117,10 +121,9 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   const int klast = st.ksteps - 1;
   const DqRegs dk = dq_regs();
   // codes of three K steps (in use, and the next two in flight); the loop is
-  // unrolled by three so every slot index is a compile-time constant. Loads
-  // are unconditional: past the last step they re-read the last step, and the
-  // DMA still targets the stage of step kt-1, which no one reads any more.
-  // Steps 0 and 1 (codes and activation stages) were issued by the caller.
+  // unrolled by three so every slot index is a compile-time constant. Steps 0
+  // and 1 (codes and activation stages) were issued by the caller; step kt
+  // issues step kt + 2 (through the empty resources once past the last step).
   u32x4_t cr[3][2] = {{cr0[0], cr0[1]}, {cr1[0], cr1[1]}, {}};
   // LDS byte address of this lane's A fragment for K slice 0 and row block 0:
   // slice ks xors its chunk index, row block rb adds rb * 4096 (the swizzle
@@ -130,13 +133,20 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   uint32_t sb0, sb1;
 
   // activations of K step src_ into ring stage stage_
-#define MOE_DMA(src_, stage_) dma_stage(st.act, st.a_off, lds, st.a_lds, (src_), (stage_))
+  // steps past the last one read through the empty resources: the loads
+  // stay in the instruction stream (so every wait count holds) but touch no
+  // memory and return zeros into a stage or code slot no one reads
+#define MOE_DMA(src_, stage_)                                                                \
+  dma_stage((src_) <= klast ? st.actr : st.actr_none, st.a_off, lds, st.a_lds,               \
+            (src_) <= klast ? (src_) : 0, (stage_))
 #define MOE_LOAD_B(kt_, slot_)                                                              \
   {                                                                                         \
+    const __amdgpu_buffer_rsrc_t r_ = (kt_) <= klast ? st.codes : st.codes_none;             \
+    const int so_ = (kt_) <= klast ? (kt_) * (kKT / 2) : 0;                                  \
     cr[slot_][0] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(       \
-                                                 st.codes, st.c_off[0], (kt_) * (kKT / 2), 0)); \
+                                                 r_, st.c_off[0], so_, 0));                  \
     cr[slot_][1] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(       \
-                                                 st.codes, st.c_off[1], (kt_) * (kKT / 2), 0)); \
+                                                 r_, st.c_off[1], so_, 0));                  \
   }
 
   // B fragments (dequantised codes) of one K slice of this lane's two weight
@@ -167,8 +177,8 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
     __builtin_amdgcn_s_barrier();                                                            \
     /* no LDS access or use of this step's codes moves above the wait and barrier */        \
     asm volatile("" : "+v"(cr[slot_][0]), "+v"(cr[slot_][1])::"memory");                    \
-    MOE_DMA(min(ktv_ + 2, klast), (ktv_ + 2) % kStages);                                     \
-    MOE_LOAD_B(min(ktv_ + 2, klast), ((slot_) + 2) % 3);                                     \
+    MOE_DMA(ktv_ + 2, (ktv_ + 2) % kStages);                                                 \
+    MOE_LOAD_B(ktv_ + 2, ((slot_) + 2) % 3);                                                 \
     const uint32_t s0_ = sb0, s1_ = sb1;                                                     \
     {                                                                                        \
       const int kn_ = min(ktv_ + 1, klast) * kWgCols + st.lr0;                               \
@@ -219,7 +229,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   }
   if (kt < st.ksteps) MOE_STEP(kt, 0);
   if (kt + 1 < st.ksteps) MOE_STEP(kt + 1, 1);
-  // no DMA may still be writing LDS when the workgroup ends
+  // no DMA may still be writing LDS when the workgroup moves on
   MOE_WAIT_VMCNT(0);
 #undef MOE_STEP
 #undef MOE_DQ
@@ -258,7 +268,13 @@ __global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
   const int TK = T * k;
 
   TileSetup st;
-  st.act = act;
+  {
+    // x: T rows of d; h: T*k routed + T shared rows of f (under 2^32 bytes)
+    const uint32_t act_bytes =
+        (uint32_t)((KIND == kGateUp ? (size_t)T : (size_t)TK + T) * (size_t)K * 2);
+    st.actr = __builtin_amdgcn_make_buffer_rsrc((void *)act, (short)0, act_bytes, 0x00020000);
+    st.actr_none = __builtin_amdgcn_make_buffer_rsrc((void *)act, (short)0, 0, 0x00020000);
+  }
   st.ksteps = K / kKT;
   const int klast = st.ksteps - 1;
   // ---- prologue. The loads go out in dependency order so that their
@@ -298,6 +314,7 @@ __global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
   const uint32_t R0 = wave_on ? (uint32_t)wrow0 : 0u, R1 = wave_on ? (uint32_t)wrow1 : 0u;
   st.codes = __builtin_amdgcn_make_buffer_rsrc((void *)(W.codes + ex * (size_t)nrows_w * (K / 2)),
                                                (short)0, nrows_w * (K / 2), 0x00020000);
+  st.codes_none = __builtin_amdgcn_make_buffer_rsrc((void *)W.codes, (short)0, 0, 0x00020000);
   st.c_off[0] = R0 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
   st.c_off[1] = R1 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
   u32x4_t cr0[2], cr1[2];
@@ -335,11 +352,11 @@ __global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
 #pragma unroll
     for (int i = 0; i < kDma; ++i) {
       const int t = KIND == kGateUp ? (tok[i] < 0 ? 0 : (tok[i] >= T ? T - 1 : tok[i])) : tok[i];
-      st.a_off[i] = (uint32_t)t * (uint32_t)K + j * 8u;  // token clamped: in range for any routing
+      st.a_off[i] = ((uint32_t)t * (uint32_t)K + j * 8u) * 2u;  // token clamped: in range for any routing
     }
   }
-  dma_stage(act, st.a_off, smem, st.a_lds, 0, 0);
-  dma_stage(act, st.a_off, smem, st.a_lds, min(1, klast), 1);
+  dma_stage(st.actr, st.a_off, smem, st.a_lds, 0, 0);
+  dma_stage(st.actr, st.a_off, smem, st.a_lds, min(1, klast), 1);
   if (vec) {
     for (int g0 = 0; g0 < ng; g0 += 32) {
       if (g0 > 0) {
