@@ -38,16 +38,20 @@
 namespace moe {
 
 constexpr int kKT = 64;                      // K per step: one quantisation group
-constexpr int kWgCols = 256;                 // weight rows per workgroup (64 per wavefront)
+constexpr int kWaves = 4;                     // wavefronts per workgroup
+constexpr int kThreads = kWaves * 64;
+constexpr int kWgCols = 64 * kWaves;         // weight rows per workgroup (64 per wavefront)
 constexpr int kRB = kBlockM / 32;            // 32-row blocks per tile
 constexpr int kStages = 3;                   // activation ring depth
 constexpr int kStageBytes = kBlockM * 128;   // one K step of the tile's rows, bf16
-constexpr int kDma = kBlockM * 8 / 256;      // 16-byte DMA chunks per thread per K step
+constexpr int kDma = kBlockM * 8 / kThreads;  // 16-byte DMA chunks per thread per K step
+constexpr int kDmaRows = kThreads / 8;        // tile rows one DMA instruction of the workgroup fills
+static_assert(kWaves % 2 == 0 && kBlockM % kDmaRows == 0, "DMA row mapping");
 constexpr int kXcds = 8;
 
 // workgroups per CU the register budget is sized for (128-row tiles leave
 // room for two; 256-row tiles need all 512 registers of a lane)
-constexpr int kOcc = kBlockM <= 128 ? 2 : 1;
+constexpr int kOcc = kBlockM <= 128 && kWaves <= 4 ? 2 : 1;
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -84,7 +88,7 @@ __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t actr,
   uint8_t *s = lds + stage * kStageBytes + a_lds;
 #pragma unroll
   for (int i = 0; i < kDma; ++i)
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(actr, (lds_void *)(s + i * 4096), 16, a_off[i],
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(actr, (lds_void *)(s + i * kDmaRows * 128), 16, a_off[i],
                                              src * (kKT * 2), 0, 0);
 }
 
@@ -238,7 +242,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
 }
 
 template <int KIND>
-__global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
+__global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
     const uint16_t *__restrict__ act, W4 wr, W4 ws, const int32_t *__restrict__ sorted_token,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ num_tiles_p,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32, int T, int d, int f, int E,
@@ -284,16 +288,17 @@ __global__ __launch_bounds__(256, kOcc) void grouped_gemm_w4_kernel(
   // flight.
   //
   // Activation rows: DMA instruction i of wavefront w fills tile rows
-  // 32 i + 8 w .. +7 (1 KB, 16 bytes per lane in lane order); lane l lands in
-  // row r = 32 i + 8 w + l / 8 at 16-byte slot l % 8, which holds logical
-  // chunk (l % 8) ^ (r % 8) ^ ((r / 8) % 2) of the row (the swizzle). Rows
+  // R i + 8 w .. +7, R = 8 x wavefronts (1 KB, 16 bytes per lane in lane
+  // order); lane l lands in row r = R i + 8 w + l / 8 at 16-byte slot l % 8,
+  // which holds logical chunk (l % 8) ^ (r % 8) ^ ((r / 8) % 2) of the row
+  // (the swizzle; (r / 8) % 2 == w % 2 as R / 8 is even). Rows
   // past the tile's end re-read its last row (their results are never
   // stored), so every load is unconditional.
   st.a_lds = (uint32_t)wave * 1024u;
   int tok[kDma];
 #pragma unroll
   for (int i = 0; i < kDma; ++i) {
-    const int p = min(row_begin + 32 * i + 8 * wave + (lane >> 3), row_end - 1);
+    const int p = min(row_begin + kDmaRows * i + 8 * wave + (lane >> 3), row_end - 1);
     tok[i] = KIND == kGateUp ? (shared ? p - TK : sorted_token[p]) : p;
   }
   // ---- this wavefront's two 32-row blocks of weight rows
@@ -490,7 +495,7 @@ static long long round_up8(long long n) { return (n + kXcds - 1) / kXcds * kXcds
 // scale/bias table (K/64 groups x 256 weight rows x 4 bytes).
 static size_t gemm_lds_bytes(int K) {
   const size_t loop = (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
-  const size_t epilogue = 4 * kBlockM * 128;  // four wavefronts x kBlockM rows x 128 bytes (down)
+  const size_t epilogue = (size_t)kWaves * kBlockM * 128;  // per wavefront kBlockM rows x 128 bytes (down)
   return loop > epilogue ? loop : epilogue;
 }
 
@@ -514,7 +519,7 @@ hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.f + kWgCols / 2 - 1) / (kWgCols / 2);
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
-  grouped_gemm_w4_kernel<kGateUp><<<grid, 256, gemm_lds_bytes(dm.d), s>>>(
+  grouped_gemm_w4_kernel<kGateUp><<<grid, kThreads, gemm_lds_bytes(dm.d), s>>>(
       x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
       dm.k);
   return hipGetLastError();
@@ -526,7 +531,7 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const Weights &w,
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.d + kWgCols - 1) / kWgCols;
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
-  grouped_gemm_w4_kernel<kDown><<<grid, 256, gemm_lds_bytes(dm.f), s>>>(
+  grouped_gemm_w4_kernel<kDown><<<grid, kThreads, gemm_lds_bytes(dm.f), s>>>(
       h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
       dm.k);
   return hipGetLastError();
