@@ -29,6 +29,10 @@ SMALL = [
     G.small_config("skew_empty_t300", T=300, d=256, f=128, E=32, k=4, seed=16, zipf_s=1.1,
                    n_forced_empty=3),
     G.small_config("multi_tile_t700", T=700, d=128, f=128, E=2, k=1, seed=17),
+    # the widest inputs the grouped GEMMs take (their LDS scale tables for
+    # K = 6144 leave room for one workgroup per CU)
+    G.small_config("max_d6144_t40", T=40, d=6144, f=64, E=3, k=2, seed=18),
+    G.small_config("max_f6144_t40", T=40, d=64, f=6144, E=3, k=2, seed=19),
 ]
 
 
