@@ -3,25 +3,33 @@
 // onde estao os ganhos": these four steps stay in one GPU submission so that
 // no CPU synchronisation happens inside an MoE layer).
 //
-// Three kernels on one stream:
-//   perm_hist    per block of 256 tokens, a per-expert count (LDS atomics);
-//   perm_scan    one workgroup: per-expert running prefix over the blocks,
-//                exclusive scan over experts (offsets), tiles per group and
-//                their exclusive scan, then the tile map, and the order the
-//                grouped GEMMs take the tiles in (fourth column: tallest
-//                first, so the longest work items start first and the short
-//                ones fill the tail of the launch);
-//   perm_scatter per block, the rank of each assignment among the block's
-//                assignments to the same expert, from a token bitmask per
-//                expert (popcount of the bits below the token), so the row
-//                order is a stable counting sort and does not depend on the
-//                order atomics happen in.
+// Two kernels on one stream, over blocks of 256 tokens:
+//   perm_hist   one workgroup per block: per-expert count of the block's
+//               assignments (LDS atomics), written to block_counts[b][E];
+//   perm_place  one workgroup per block, plus one more. Every workgroup
+//               redoes the small scan it needs from block_counts (per-expert
+//               total and count over the earlier blocks, exclusive scan over
+//               experts), so no third launch has to wait for a global scan.
+//               A block workgroup then scatters its tokens: the rank of an
+//               assignment among the block's assignments to the same expert
+//               comes from a token bitmask per expert (popcount of the bits
+//               below the token), so the row order is a stable counting sort
+//               and does not depend on the order atomics happen in. The
+//               extra workgroup writes counts, offsets, the tile map and the
+//               order the grouped GEMMs take the tiles in (fourth column:
+//               tallest first, so the longest work items start first and the
+//               short ones fill the tail of the launch).
 #include "moe_launch.h"
 
 namespace moe {
 
 constexpr int kMaxExperts = 1024;
 constexpr int kMaskWords = kPermTokens / 32;
+constexpr int kPlaceThreads = 1024;
+// assignments of one token block per thread: kPermTokens * k / kPlaceThreads, k <= 32
+constexpr int kPerThread = kPermTokens * 32 / kPlaceThreads;
+// block counts each thread loads at once
+constexpr int kChunk = 16;
 
 __device__ __forceinline__ int clamp_id(int e, int E) { return e < 0 ? 0 : (e >= E ? E - 1 : e); }
 
@@ -32,9 +40,18 @@ __global__ __launch_bounds__(256) void perm_hist_kernel(const int32_t *__restric
   for (int e = threadIdx.x; e < E; e += blockDim.x) cnt[e] = 0;
   __syncthreads();
   const int t0 = blockIdx.x * kPermTokens;
-  const int nt = min(kPermTokens, T - t0);
+  const int na = min(kPermTokens, T - t0) * k;
   const int32_t *blk = ids + (size_t)t0 * k;
-  for (int a = threadIdx.x; a < nt * k; a += blockDim.x) atomicAdd(&cnt[clamp_id(blk[a], E)], 1);
+  // up to 32 ids per thread (k <= 32), all loaded before the atomics
+  int v[32];
+#pragma unroll
+  for (int i = 0; i < 32; ++i) {
+    const int a = threadIdx.x + i * 256;
+    v[i] = a < na ? blk[a] : -1;
+  }
+#pragma unroll
+  for (int i = 0; i < 32; ++i)
+    if (threadIdx.x + i * 256 < na) atomicAdd(&cnt[clamp_id(v[i], E)], 1);
   __syncthreads();
   for (int e = threadIdx.x; e < E; e += blockDim.x)
     block_counts[(size_t)blockIdx.x * E + e] = cnt[e];
@@ -74,41 +91,31 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *wave_tot) {
 constexpr int kMaxGroups = kMaxExperts + 1;
 constexpr int kGroupWords = (kMaxGroups + 31) / 32;
 
-__global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ block_counts,
-                                                         int nblocks, int T, int E, int k,
-                                                         int32_t *__restrict__ counts,
-                                                         int32_t *__restrict__ offsets,
-                                                         int32_t *__restrict__ tile_map,
-                                                         int32_t *__restrict__ num_tiles) {
-  __shared__ int wave_tot[16];
-  __shared__ int s_routed_tiles, s_routed_full;
-  __shared__ uint32_t hmask[kBlockM][kGroupWords];  // groups whose partial tile has height r
-  __shared__ int hstart[kBlockM];                   // schedule position of height r's first tile
+struct PlaceLds {
+  int wave_tot[16];
+  int routed_tiles, routed_full;
+  union {
+    struct {
+      int off[kMaxExperts];                   // first row of the block's assignments per expert
+      uint32_t mask[kMaxExperts * kMaskWords];  // per expert: tokens of the block
+    } s;
+    struct {
+      uint32_t hmask[kBlockM][kGroupWords];  // groups whose partial tile has height r
+      int hstart[kBlockM];                   // schedule position of height r's first tile
+    } m;
+  } u;
+};
+
+// Tile map, counts and offsets (the extra workgroup). Thread e owns expert e.
+__device__ void write_tile_map(PlaceLds &L, int c, int c_incl, int T, int E, int k,
+                               int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+                               int32_t *__restrict__ tile_map, int32_t *__restrict__ num_tiles) {
   const int e = threadIdx.x;
-  for (int i = e; i < kBlockM * kGroupWords; i += blockDim.x) (&hmask[0][0])[i] = 0u;
-  // per-expert running prefix over token blocks, in place; the counts of 16
-  // blocks are loaded together before any is overwritten (a load after a
-  // store to the same array would otherwise wait for a full round trip each)
-  int c = 0;
-  if (e < E) {
-    constexpr int kChunk = 16;
-    for (int b0 = 0; b0 < nblocks; b0 += kChunk) {
-      int v[kChunk];
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i)
-        v[i] = b0 + i < nblocks ? block_counts[(size_t)(b0 + i) * E + e] : 0;
-#pragma unroll
-      for (int i = 0; i < kChunk; ++i) {
-        if (b0 + i < nblocks) block_counts[(size_t)(b0 + i) * E + e] = c;
-        c += v[i];
-      }
-    }
-  }
+  for (int i = e; i < kBlockM * kGroupWords; i += kPlaceThreads) (&L.u.m.hmask[0][0])[i] = 0u;
   const int nt = (c + kBlockM - 1) / kBlockM;
   const int nf = c / kBlockM;  // full tiles
-  const int c_incl = block_inclusive_scan(c, wave_tot);
-  const int nt_incl = block_inclusive_scan(nt, wave_tot);
-  const int nf_incl = block_inclusive_scan(nf, wave_tot);
+  const int nt_incl = block_inclusive_scan(nt, L.wave_tot);
+  const int nf_incl = block_inclusive_scan(nf, L.wave_tot);
   const int off = c_incl - c;
   const int tbase = nt_incl - nt;
   const int fbase = nf_incl - nf;
@@ -123,19 +130,19 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
       row[1] = rb;
       row[2] = re;
     }
-    if (c % kBlockM) atomicOr(&hmask[c % kBlockM][e >> 5], 1u << (e & 31));
+    if (c % kBlockM) atomicOr(&L.u.m.hmask[c % kBlockM][e >> 5], 1u << (e & 31));
   }
-  if (e == blockDim.x - 1) {
+  if (e == kPlaceThreads - 1) {
     offsets[E] = c_incl;  // == T*k
-    s_routed_tiles = nt_incl;
-    s_routed_full = nf_incl;
+    L.routed_tiles = nt_incl;
+    L.routed_full = nf_incl;
   }
   __syncthreads();
   // the shared group E: rows T*k .. T*k+T-1
-  const int rbase = s_routed_tiles;
+  const int rbase = L.routed_tiles;
   const int ns = (T + kBlockM - 1) / kBlockM;
   const int sh0 = T * k;
-  for (int i = e; i < ns; i += blockDim.x) {
+  for (int i = e; i < ns; i += kPlaceThreads) {
     const int rb = sh0 + i * kBlockM;
     const int re = min(rb + kBlockM, sh0 + T);
     int32_t *row = tile_map + 4 * (size_t)(rbase + i);
@@ -145,65 +152,106 @@ __global__ __launch_bounds__(1024) void perm_scan_kernel(int32_t *__restrict__ b
   }
   if (e == 0) {
     *num_tiles = rbase + ns;
-    if (T % kBlockM) atomicOr(&hmask[T % kBlockM][E >> 5], 1u << (E & 31));
+    if (T % kBlockM) atomicOr(&L.u.m.hmask[T % kBlockM][E >> 5], 1u << (E & 31));
   }
   __syncthreads();
   // tiles per height, then the first schedule position of each height
   // (heights kBlockM-1 .. 1 after all full tiles)
-  const int nfull = s_routed_full + T / kBlockM;
+  const int nfull = L.routed_full + T / kBlockM;
   int hc = 0;
   const int hgt = kBlockM - 1 - e;  // thread e counts height kBlockM-1-e (e < kBlockM-1)
   if (e < kBlockM - 1)
-    for (int w = 0; w < kGroupWords; ++w) hc += __popc(hmask[hgt][w]);
-  const int hc_incl = block_inclusive_scan(e < kBlockM - 1 ? hc : 0, wave_tot);
-  if (e < kBlockM - 1) hstart[hgt] = nfull + hc_incl - hc;
+    for (int w = 0; w < kGroupWords; ++w) hc += __popc(L.u.m.hmask[hgt][w]);
+  const int hc_incl = block_inclusive_scan(e < kBlockM - 1 ? hc : 0, L.wave_tot);
+  if (e < kBlockM - 1) L.u.m.hstart[hgt] = nfull + hc_incl - hc;
   __syncthreads();
   // schedule entries: full routed tiles, full shared tiles, partial tiles
   if (e < E) {
     for (int i = 0; i < nf; ++i) tile_map[4 * (size_t)(fbase + i) + 3] = tbase + i;
     const int r = c % kBlockM;
     if (r) {
-      int rank = __popc(hmask[r][e >> 5] & ((1u << (e & 31)) - 1u));
-      for (int w = 0; w < (e >> 5); ++w) rank += __popc(hmask[r][w]);
-      tile_map[4 * (size_t)(hstart[r] + rank) + 3] = tbase + nf;
+      int rank = __popc(L.u.m.hmask[r][e >> 5] & ((1u << (e & 31)) - 1u));
+      for (int w = 0; w < (e >> 5); ++w) rank += __popc(L.u.m.hmask[r][w]);
+      tile_map[4 * (size_t)(L.u.m.hstart[r] + rank) + 3] = tbase + nf;
     }
   }
-  for (int i = e; i < T / kBlockM; i += blockDim.x)
-    tile_map[4 * (size_t)(s_routed_full + i) + 3] = rbase + i;
+  for (int i = e; i < T / kBlockM; i += kPlaceThreads)
+    tile_map[4 * (size_t)(L.routed_full + i) + 3] = rbase + i;
   if (e == 0 && T % kBlockM) {
     const int r = T % kBlockM;
     int rank = 0;
     for (int w = 0; w <= (E >> 5); ++w)
-      rank += __popc(w < (E >> 5) ? hmask[r][w] : (hmask[r][w] & ((1u << (E & 31)) - 1u)));
-    tile_map[4 * (size_t)(hstart[r] + rank) + 3] = rbase + ns - 1;
+      rank += __popc(w < (E >> 5) ? L.u.m.hmask[r][w]
+                                  : (L.u.m.hmask[r][w] & ((1u << (E & 31)) - 1u)));
+    tile_map[4 * (size_t)(L.u.m.hstart[r] + rank) + 3] = rbase + ns - 1;
   }
 }
 
-__global__ __launch_bounds__(kPermTokens) void perm_scatter_kernel(
-    const int32_t *__restrict__ ids, int T, int E, int k, const int32_t *__restrict__ offsets,
-    const int32_t *__restrict__ block_prefix, int32_t *__restrict__ sorted_token,
-    int32_t *__restrict__ row_of) {
-  __shared__ uint32_t mask[kMaxExperts * kMaskWords];
-  for (int i = threadIdx.x; i < E * kMaskWords; i += blockDim.x) mask[i] = 0u;
+__global__ __launch_bounds__(kPlaceThreads) void perm_place_kernel(
+    const int32_t *__restrict__ ids, const int32_t *__restrict__ block_counts, int nblocks, int T,
+    int E, int k, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ row_of,
+    int32_t *__restrict__ tile_map, int32_t *__restrict__ num_tiles) {
+  __shared__ PlaceLds L;
+  const int tid = threadIdx.x;
+  const int b = blockIdx.x;  // token block, or nblocks for the tile-map workgroup
+  const bool mapper = b == nblocks;
+  const int t0 = b * kPermTokens;
+  const int na = mapper ? 0 : min(kPermTokens, T - t0) * k;  // assignments of this block
+  // the block's ids, in flight while the counts are scanned
+  int cur[kPerThread];
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int a = tid + i * kPlaceThreads;
+    cur[i] = a < na ? clamp_id(ids[(size_t)t0 * k + a], E) : 0;
+  }
+  if (!mapper)
+    for (int i = tid; i < E * kMaskWords; i += kPlaceThreads) L.u.s.mask[i] = 0u;
+  // thread e: total of expert e and its count over the blocks before b
+  const int e = tid;
+  int c = 0, before = 0;
+  if (e < E) {
+    for (int b0 = 0; b0 < nblocks; b0 += kChunk) {
+      int v[kChunk];
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i)
+        v[i] = b0 + i < nblocks ? block_counts[(size_t)(b0 + i) * E + e] : 0;
+#pragma unroll
+      for (int i = 0; i < kChunk; ++i) {
+        if (b0 + i == b) before = c;
+        c += v[i];
+      }
+    }
+  }
+  const int c_incl = block_inclusive_scan(c, L.wave_tot);
+  if (mapper) {
+    write_tile_map(L, c, c_incl, T, E, k, counts, offsets, tile_map, num_tiles);
+    return;
+  }
+  if (e < E) L.u.s.off[e] = c_incl - c + before;
+  // the block's token bitmask per expert (the scan's barriers ordered the
+  // clearing of mask before these)
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int a = tid + i * kPlaceThreads;
+    if (a < na) {
+      const int tl = a / k;
+      atomicOr(&L.u.s.mask[cur[i] * kMaskWords + (tl >> 5)], 1u << (tl & 31));
+    }
+  }
   __syncthreads();
-  const int tl = threadIdx.x;
-  const int t = blockIdx.x * kPermTokens + tl;
-  const bool valid = t < T;
-  const int word = tl >> 5;
-  const uint32_t bit = 1u << (tl & 31);
-  if (valid)
-    for (int j = 0; j < k; ++j) atomicOr(&mask[clamp_id(ids[(size_t)t * k + j], E) * kMaskWords + word], bit);
-  __syncthreads();
-  if (!valid) return;
-  const int32_t *pre = block_prefix + (size_t)blockIdx.x * E;
-  for (int j = 0; j < k; ++j) {
-    const int e = clamp_id(ids[(size_t)t * k + j], E);
-    const uint32_t *m = mask + e * kMaskWords;
-    int rank = __popc(m[word] & (bit - 1u));
-    for (int w = 0; w < word; ++w) rank += __popc(m[w]);
-    const int p = offsets[e] + pre[e] + rank;
-    sorted_token[p] = t;
-    row_of[(size_t)t * k + j] = p;
+#pragma unroll
+  for (int i = 0; i < kPerThread; ++i) {
+    const int a = tid + i * kPlaceThreads;
+    if (a < na) {
+      const int tl = a / k, ex = cur[i];
+      const uint32_t *m = L.u.s.mask + ex * kMaskWords;
+      int rank = __popc(m[tl >> 5] & ((1u << (tl & 31)) - 1u));
+      for (int w = 0; w < (tl >> 5); ++w) rank += __popc(m[w]);
+      const int p = L.u.s.off[ex] + rank;
+      sorted_token[p] = t0 + tl;
+      row_of[(size_t)t0 * k + a] = p;
+    }
   }
 }
 
@@ -212,10 +260,9 @@ hipError_t launch_permute(const Dims &dm, const int32_t *ids, int32_t *counts, i
                           int32_t *num_tiles, int32_t *block_counts, hipStream_t s) {
   const int nb = perm_blocks(dm.T);
   perm_hist_kernel<<<nb, 256, 0, s>>>(ids, dm.T, dm.E, dm.k, block_counts);
-  perm_scan_kernel<<<1, 1024, 0, s>>>(block_counts, nb, dm.T, dm.E, dm.k, counts, offsets,
-                                      tile_map, num_tiles);
-  perm_scatter_kernel<<<nb, kPermTokens, 0, s>>>(ids, dm.T, dm.E, dm.k, offsets, block_counts,
-                                                 sorted_token, row_of);
+  perm_place_kernel<<<nb + 1, kPlaceThreads, 0, s>>>(ids, block_counts, nb, dm.T, dm.E, dm.k,
+                                                    counts, offsets, sorted_token, row_of,
+                                                    tile_map, num_tiles);
   return hipGetLastError();
 }
 
