@@ -53,6 +53,7 @@ TAG_S2_CODES = 22
 TAG_S2_SCALES = 23
 TAG_DEC_X = 30
 TAG_DEC_LOGITS = 31
+TAG_ROUTER = 40
 
 
 @dataclasses.dataclass(frozen=True)
@@ -129,6 +130,13 @@ def make_weights(cfg: MoeConfig) -> Dict[str, Dict[str, np.ndarray]]:
         "s13": make_w4(s, TAG_S13_CODES, TAG_S13_SCALES, 1, 2 * cfg.f_shared, cfg.d, lo, hi),
         "s2": make_w4(s, TAG_S2_CODES, TAG_S2_SCALES, 1, cfg.d, cfg.f_shared, lo, hi),
     }
+
+
+def make_router(cfg: MoeConfig) -> np.ndarray:
+    """Router matrix Wr, bf16 bits [E, d], entries N(0, 1/d): with N(0, 1) hidden
+    states the scores come out near N(0, 1), like the logits of the other workloads."""
+    w = rng(cfg.seed, TAG_ROUTER).standard_normal((cfg.E, cfg.d)) / np.sqrt(cfg.d)
+    return f32_to_bf16_bits(w.astype(np.float32))
 
 
 def zipf_bias(cfg: MoeConfig) -> np.ndarray:

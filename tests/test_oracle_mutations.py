@@ -91,6 +91,18 @@ def pin_group_extent(M):
     assert (w[0, :64] == 3).all() and (w[0, 64:128] == 6).all() and (w[0, 192:] == 24).all()
 
 
+def pin_router(M):
+    r = np.random.default_rng(6)
+    T, d, E = 5, 128, 7
+    x = r.standard_normal((T, d)).astype(np.float32)
+    xb = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    perm = r.permutation(d)[:E]
+    w = np.zeros((E, d), np.float32)
+    w[np.arange(E), perm] = 1.0
+    wb = torch.from_numpy(w).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
+    assert np.array_equal(M.router_logits(xb, wb), M.bf16_to_f64(xb)[:, perm])
+
+
 MUTATIONS = [
     ("nibble order swapped", "q[..., 0::2] = codes & np.uint8(0x0F)", "q[..., 0::2] = codes >> np.uint8(4)", pin_dequant),
     ("bias sign flipped", "w32 = (s * q) + b", "w32 = (s * q) - b", pin_dequant),
@@ -110,6 +122,10 @@ MUTATIONS = [
     ("scatter not stable", "for t in range(T):", "for t in reversed(range(T)):", pin_permutation),
     ("last tile not clipped", "tiles.append((g, off + i * BM, min(off + (i + 1) * BM, off + c)))",
      "tiles.append((g, off + i * BM, off + (i + 1) * BM))", pin_block_map),
+    ("router experts in reverse order", "return bf16_to_f64(x_bits) @ bf16_to_f64(wr_bits).T",
+     "return bf16_to_f64(x_bits) @ bf16_to_f64(wr_bits)[::-1].T", pin_router),
+    ("router drops a column group", "return bf16_to_f64(x_bits) @ bf16_to_f64(wr_bits).T",
+     "return bf16_to_f64(x_bits)[:, 64:] @ bf16_to_f64(wr_bits)[:, 64:].T", pin_router),
 ]
 
 
