@@ -183,6 +183,24 @@ def main():
     kernels["down"]["TFLOP/s"] = round(flop_down / (acc["down"] / 1e3) / 1e12, 1)
     comb_bytes = T * k * d * 2 + T * d * 4 * 2 + T * k * 8
     kernels["combine"]["GB/s"] = round(comb_bytes / (acc["combine"] / 1e3) / 1e9, 1)
+    # router projection (the step before routing when the layer starts from
+    # hidden states); timed on its own, the headline step starts from logits
+    wr = torch.from_numpy(G.make_router(cfg).view(np.int16)).to(dev)
+    lg = torch.empty((T, E), dtype=torch.float32, device=dev)
+    M.moe_router_logits(x, wr, logits=lg, stream=stream)
+    rev = []
+    for it in range(n_iter + 2):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record(stream)
+        M.moe_router_logits(x, wr, logits=lg, stream=stream)
+        ev[1].record(stream)
+        if it >= 2:
+            rev.append(ev)
+    torch.cuda.synchronize()
+    us = sum(a.elapsed_time(b) for a, b in rev) / len(rev) * 1e3
+    kernels["router_logits"] = {"us": round(us, 2),
+                                "TFLOP/s": round(2.0 * T * d * E / (us / 1e6) / 1e12, 1),
+                                "GB/s": round((T * d * 2 + E * d * 2 + T * E * 4) / (us / 1e6) / 1e9, 1)}
     log(f"[bench] kernels: {kernels}")
     achieved = flop_gate_up / (acc["gate_up"] / 1e3) / 1e12
     roofline = {"kernel": "gate_up_kernel", "bound": "mfma", "achieved": round(achieved, 2),

@@ -22,7 +22,8 @@ EXPORTS = [
     "moe_route", "moe_block_m", "moe_tile_capacity", "moe_permute_workspace_bytes",
     "moe_permute", "moe_expert_gate_up_w4", "moe_expert_down_w4", "moe_expert_ffn_w4",
     "moe_unpermute_combine", "moe_layer_workspace_bytes", "moe_layer_forward",
-    "moe_dequant_w4", "moe_status_string", "moe_last_hip_error",
+    "moe_dequant_w4", "moe_status_string", "moe_last_hip_error", "moe_router_logits",
+    "moe_layer_forward_hidden",
 ]
 
 
@@ -70,6 +71,8 @@ def lib() -> ctypes.CDLL:
             "moe_unpermute_combine": ([D, P, P, P, P, P, P], I32),
             "moe_layer_workspace_bytes": ([D], SZ),
             "moe_layer_forward": ([D, P, P, W, P, P, SZ, P], I32),
+            "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
+            "moe_layer_forward_hidden": ([D, P, P, W, P, P, SZ, P], I32),
             "moe_dequant_w4": ([ctypes.POINTER(MoeW4Matrix), I32, I32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
             "moe_last_hip_error": ([], I32),
@@ -253,6 +256,31 @@ def moe_layer_forward(dm: MoeDims, x: torch.Tensor, logits: torch.Tensor, w: W4W
     _check(lib().moe_layer_forward(ctypes.byref(dm), _ptr(x), _ptr(logits), ctypes.byref(wc),
                                    _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor, logits=None, stream=None):
+    """logits [T, E] fp32 = x [T, d] (bf16) times w_router [E, d] (bf16) transposed."""
+    T, d = x.shape
+    E = w_router.shape[0]
+    if logits is None:
+        logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _check(lib().moe_router_logits(_ptr(x), _ptr(w_router), T, d, E, _ptr(logits),
+                                   _stream(stream)), "moe_router_logits")
+    return logits
+
+
+def moe_layer_forward_hidden(dm: MoeDims, x: torch.Tensor, w_router: torch.Tensor, w: W4Weights,
+                             y=None, ws=None, stream=None, wc: Optional[MoeW4Weights] = None):
+    """One layer call from hidden states (router projection included)."""
+    if y is None:
+        y = torch.empty((dm.T, dm.d), dtype=torch.float32, device=x.device)
+    if ws is None:
+        ws = torch.empty(max(moe_layer_workspace_bytes(dm), 16), dtype=torch.uint8, device=x.device)
+    wc = w.c() if wc is None else wc
+    _check(lib().moe_layer_forward_hidden(ctypes.byref(dm), _ptr(x), _ptr(w_router),
+                                          ctypes.byref(wc), _ptr(y), _ptr(ws), ws.numel(),
+                                          _stream(stream)), "moe_layer_forward_hidden")
     return y
 
 

@@ -69,6 +69,17 @@ moe_status check_weights(const moe_w4_weights *w, bool up, bool down) {
   return MOE_OK;
 }
 
+// Shapes the router projection takes: d a multiple of 64 (one K step), E up to
+// 1024, and x, Wr and the logits each under 2^31 elements.
+moe_status check_router_dims(int32_t T, int32_t d, int32_t E) {
+  if (T < 0 || d <= 0 || E <= 0) return MOE_E_INVALID;
+  if (d % kGroup != 0 || E > 1024) return MOE_E_UNSUPPORTED;
+  if ((long long)T * d >= (1ll << 31) || (long long)E * d >= (1ll << 31) ||
+      (long long)T * E >= (1ll << 31))
+    return MOE_E_UNSUPPORTED;
+  return MOE_OK;
+}
+
 Dims to_dims(const moe_dims *dm) { return Dims{dm->T, dm->d, dm->f, dm->E, dm->k}; }
 
 W4 to_w4(const moe_w4_matrix &m) { return W4{m.codes, m.scales, m.biases}; }
@@ -84,7 +95,7 @@ size_t align256(size_t n) { return (n + 255) & ~(size_t)255; }
 // Carving of the layer workspace. With base == nullptr only sizes are computed.
 struct LayerWs {
   int32_t *ids, *counts, *offsets, *sorted_token, *row_of, *tile_map, *num_tiles, *block_counts;
-  float *wts, *o_shared;
+  float *wts, *o_shared, *logits;
   uint16_t *h, *o_routed;
   size_t bytes;
 };
@@ -112,6 +123,7 @@ LayerWs carve_layer(const Dims &dm, char *base) {
   w.h = take<uint16_t>(base, off, (tk + dm.T) * (size_t)dm.f);
   w.o_routed = take<uint16_t>(base, off, tk * (size_t)dm.d);
   w.o_shared = take<float>(base, off, (size_t)dm.T * dm.d);
+  w.logits = take<float>(base, off, (size_t)dm.T * dm.E);  // router scores (hidden-state entry)
   w.bytes = off;
   return w;
 }
@@ -238,6 +250,19 @@ moe_status moe_unpermute_combine(const moe_dims *dm, const uint16_t *o_routed,
       launch_combine(to_dims(dm), o_routed, o_shared, topk_w, row_of, y, as_stream(stream)));
 }
 
+// The layer from logits on; arguments already validated.
+static moe_status enqueue_layer(const Dims &d, const uint16_t *x, const float *logits, const Weights &W,
+                         float *y, const LayerWs &L, hipStream_t s) {
+  if (decode_supported(d))
+    return hip_status(launch_decode(d, x, logits, W, L.ids, L.wts, L.h, y, s));
+  MOE_TRY(hip_status(launch_route(logits, d.T, d.E, d.k, L.ids, L.wts, s)));
+  MOE_TRY(hip_status(launch_permute(d, L.ids, L.counts, L.offsets, L.sorted_token, L.row_of,
+                                    L.tile_map, L.num_tiles, L.block_counts, s)));
+  MOE_TRY(hip_status(launch_gate_up(d, x, W, L.sorted_token, L.tile_map, L.num_tiles, L.h, s)));
+  MOE_TRY(hip_status(launch_down(d, L.h, W, L.tile_map, L.num_tiles, L.o_routed, L.o_shared, s)));
+  return hip_status(launch_combine(d, L.o_routed, L.o_shared, L.wts, L.row_of, y, s));
+}
+
 moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float *logits,
                              const moe_w4_weights *w, float *y, void *ws, size_t ws_bytes,
                              void *stream) {
@@ -251,16 +276,36 @@ moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float 
   const Dims d = to_dims(dm);
   const LayerWs L = carve_layer(d, (char *)ws);
   if (ws_bytes < L.bytes) return MOE_E_WORKSPACE;
-  const Weights W = to_weights(w);
+  return enqueue_layer(d, x, logits, to_weights(w), y, L, as_stream(stream));
+}
+
+moe_status moe_router_logits(const uint16_t *x, const uint16_t *w_router, int32_t T, int32_t d,
+                             int32_t E, float *logits, void *stream) {
+  MOE_TRY(check_router_dims(T, d, E));
+  if (T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(x));
+  MOE_TRY(check_ptr(w_router));
+  MOE_TRY(check_ptr(logits));
+  return hip_status(launch_router_logits(x, w_router, T, d, E, logits, as_stream(stream)));
+}
+
+moe_status moe_layer_forward_hidden(const moe_dims *dm, const uint16_t *x,
+                                    const uint16_t *w_router, const moe_w4_weights *w, float *y,
+                                    void *ws, size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dm));
+  if (dm->T == 0) return MOE_OK;
+  MOE_TRY(check_router_dims(dm->T, dm->d, dm->E));
+  MOE_TRY(check_weights(w, true, true));
+  MOE_TRY(check_ptr(x));
+  MOE_TRY(check_ptr(w_router));
+  MOE_TRY(check_ptr(y));
+  MOE_TRY(check_ptr(ws));
+  const Dims d = to_dims(dm);
+  const LayerWs L = carve_layer(d, (char *)ws);
+  if (ws_bytes < L.bytes) return MOE_E_WORKSPACE;
   const hipStream_t s = as_stream(stream);
-  if (decode_supported(d))
-    return hip_status(launch_decode(d, x, logits, W, L.ids, L.wts, L.h, y, s));
-  MOE_TRY(hip_status(launch_route(logits, d.T, d.E, d.k, L.ids, L.wts, s)));
-  MOE_TRY(hip_status(launch_permute(d, L.ids, L.counts, L.offsets, L.sorted_token, L.row_of,
-                                    L.tile_map, L.num_tiles, L.block_counts, s)));
-  MOE_TRY(hip_status(launch_gate_up(d, x, W, L.sorted_token, L.tile_map, L.num_tiles, L.h, s)));
-  MOE_TRY(hip_status(launch_down(d, L.h, W, L.tile_map, L.num_tiles, L.o_routed, L.o_shared, s)));
-  return hip_status(launch_combine(d, L.o_routed, L.o_shared, L.wts, L.row_of, y, s));
+  MOE_TRY(hip_status(launch_router_logits(x, w_router, d.T, d.d, d.E, L.logits, s)));
+  return enqueue_layer(d, x, L.logits, to_weights(w), y, L, s);
 }
 
 moe_status moe_dequant_w4(const moe_w4_matrix *m, int32_t rows, int32_t cols, uint16_t *out,

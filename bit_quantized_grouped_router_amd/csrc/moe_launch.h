@@ -40,6 +40,9 @@ inline int perm_blocks(int T) { return (T + kPermTokens - 1) / kPermTokens; }
 hipError_t launch_route(const float *logits, int T, int E, int k, int32_t *ids, float *wts,
                         hipStream_t s);
 
+hipError_t launch_router_logits(const uint16_t *x, const uint16_t *wr, int T, int d, int E,
+                                float *logits, hipStream_t s);
+
 // block_counts: scratch int32 [perm_blocks(T)][E]
 hipError_t launch_permute(const Dims &dm, const int32_t *ids, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_token, int32_t *row_of, int32_t *tile_map,

@@ -92,6 +92,24 @@ typedef struct {
 } moe_w4_weights;
 
 /*
+ * moe_router_logits - the router's score of every expert for every token
+ * (page section "O modelo em tres formatos de carga": the router scores the
+ * E experts), as a bias-free projection of the hidden states:
+ *   logits[t][e] = sum_c x[t][c] * w_router[e][c]
+ * Products of two bf16 values are exact in fp32; they are summed in fp32 on
+ * the matrix cores (the summation order is unspecified, so results may differ
+ * from another fp32 order by rounding, within d * 2^-24 * sum_c |x w|).
+ *   x         bf16 [T][d]   hidden states
+ *   w_router  bf16 [E][d]   router matrix
+ *   logits    fp32 [T][E]   out
+ * Limits: T >= 0, d % 64 == 0, 1 <= E <= 1024, and T*d, E*d and T*E each
+ * under 2^31 (MOE_E_INVALID for negative or zero sizes, MOE_E_UNSUPPORTED
+ * past the limits).
+ */
+moe_status moe_router_logits(const uint16_t *x, const uint16_t *w_router, int32_t T, int32_t d,
+                             int32_t E, float *logits, void *stream);
+
+/*
  * moe_route - top-k selection and router weights
  * (page section "O modelo em tres formatos de carga": score E experts, keep k).
  *   logits   fp32  [T][E]  router logits
@@ -189,7 +207,8 @@ moe_status moe_unpermute_combine(const moe_dims *dm, const uint16_t *o_routed,
                                  const float *o_shared, const float *topk_w,
                                  const int32_t *row_of, float *y, void *stream);
 
-/* Bytes of workspace moe_layer_forward needs for these dims. */
+/* Bytes of workspace moe_layer_forward and moe_layer_forward_hidden need for
+ * these dims. */
 size_t moe_layer_workspace_bytes(const moe_dims *dm);
 
 /*
@@ -206,6 +225,20 @@ size_t moe_layer_workspace_bytes(const moe_dims *dm);
 moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float *logits,
                              const moe_w4_weights *w, float *y, void *ws, size_t ws_bytes,
                              void *stream);
+
+/*
+ * moe_layer_forward_hidden - moe_layer_forward starting from hidden states:
+ * moe_router_logits into the workspace, then the layer on those logits (the
+ * same kernels, T == 1 included). Every argument is validated before the
+ * first launch.
+ *   x         bf16 [T][d]
+ *   w_router  bf16 [E][d]
+ *   y         fp32 [T][d] out
+ *   ws        >= moe_layer_workspace_bytes(dm) bytes of device scratch
+ */
+moe_status moe_layer_forward_hidden(const moe_dims *dm, const uint16_t *x,
+                                    const uint16_t *w_router, const moe_w4_weights *w, float *y,
+                                    void *ws, size_t ws_bytes, void *stream);
 
 /*
  * moe_dequant_w4 - rebuild one int4-g64 matrix to bf16 with the same device

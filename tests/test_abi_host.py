@@ -145,6 +145,37 @@ def test_permute_and_ffn_validation(L):
     assert L.moe_dequant_w4(None, 4, 128, FAKE, None) == INVALID
 
 
+def test_router_validation(L):
+    r = L.moe_router_logits
+    assert r(None, None, 0, 64, 8, None, None) == OK                   # T == 0: no-op
+    assert r(FAKE, FAKE, -1, 64, 8, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 4, 0, 8, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 4, 64, 0, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 4, 100, 8, FAKE, None) == UNSUPPORTED         # d % 64 != 0
+    assert r(FAKE, FAKE, 4, 64, 1025, FAKE, None) == UNSUPPORTED
+    assert r(FAKE, FAKE, 1 << 19, 4096, 8, FAKE, None) == UNSUPPORTED   # T*d = 2^31
+    assert r(None, FAKE, 4, 64, 8, FAKE, None) == INVALID
+    assert r(FAKE, FAKE, 4, 64, 8, None, None) == INVALID
+    assert r(FAKE, FAKE + 8, 4, 64, 8, FAKE, None) == ALIGN
+
+
+def test_layer_forward_hidden_validation(L):
+    w = _weights()
+    dm = _dims()
+    need = L.moe_layer_workspace_bytes(ctypes.byref(dm))
+    fh = L.moe_layer_forward_hidden
+    assert fh(ctypes.byref(_dims(T=0)), None, None, ctypes.byref(w), None, None, 0, None) == OK
+    assert fh(ctypes.byref(_dims(d=100)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
+    assert fh(ctypes.byref(dm), FAKE, None, ctypes.byref(w), FAKE, FAKE, need, None) == INVALID
+    assert fh(ctypes.byref(dm), FAKE, FAKE + 4, ctypes.byref(w), FAKE, FAKE, need, None) == ALIGN
+    assert fh(ctypes.byref(dm), FAKE, FAKE, None, FAKE, FAKE, need, None) == INVALID
+    assert fh(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need - 1, None) == WORKSPACE
+    # the workspace holds the router scores too: it grows with E
+    a = L.moe_layer_workspace_bytes(ctypes.byref(_dims(T=64, E=8)))
+    b = L.moe_layer_workspace_bytes(ctypes.byref(_dims(T=64, E=64)))
+    assert b >= a + 64 * 56 * 4
+
+
 def test_binding_refuses_cpu_tensors(L):
     import torch
     with pytest.raises(M.MoeError):
