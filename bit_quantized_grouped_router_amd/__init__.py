@@ -23,7 +23,7 @@ EXPORTS = [
     "moe_permute", "moe_expert_gate_up_w4", "moe_expert_down_w4", "moe_expert_ffn_w4",
     "moe_unpermute_combine", "moe_layer_workspace_bytes", "moe_layer_forward",
     "moe_dequant_w4", "moe_status_string", "moe_last_hip_error", "moe_router_logits",
-    "moe_layer_forward_hidden",
+    "moe_layer_forward_hidden", "moe_route_permute",
 ]
 
 
@@ -73,6 +73,7 @@ def lib() -> ctypes.CDLL:
             "moe_layer_forward": ([D, P, P, W, P, P, SZ, P], I32),
             "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
             "moe_layer_forward_hidden": ([D, P, P, W, P, P, SZ, P], I32),
+            "moe_route_permute": ([D, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
             "moe_dequant_w4": ([ctypes.POINTER(MoeW4Matrix), I32, I32, P, P], I32),
             "moe_status_string": ([I32], ctypes.c_char_p),
             "moe_last_hip_error": ([], I32),
@@ -194,6 +195,30 @@ def moe_permute(dm: MoeDims, topk_ids: torch.Tensor, out: Optional[Dict] = None,
                              _ptr(out["offsets"]), _ptr(out["sorted_token"]),
                              _ptr(out["row_of"]), _ptr(out["tile_map"]), _ptr(out["num_tiles"]),
                              _ptr(ws), ws.numel(), _stream(stream)), "moe_permute")
+    return out
+
+
+def moe_route_permute(dm: MoeDims, logits: torch.Tensor, out: Optional[Dict] = None, ws=None,
+                      stream=None) -> Dict[str, torch.Tensor]:
+    """moe_route then moe_permute in one call; returns ids, wts and the permutation."""
+    dev = logits.device
+    tk = dm.T * dm.k
+    if out is None:
+        i32 = dict(dtype=torch.int32, device=dev)
+        out = {"ids": torch.empty((dm.T, dm.k), **i32),
+               "wts": torch.empty((dm.T, dm.k), dtype=torch.float32, device=dev),
+               "counts": torch.empty(dm.E, **i32), "offsets": torch.empty(dm.E + 1, **i32),
+               "sorted_token": torch.empty(max(tk, 1), **i32),
+               "row_of": torch.empty(max(tk, 1), **i32),
+               "tile_map": torch.empty((max(moe_tile_capacity(dm), 1), 4), **i32),
+               "num_tiles": torch.zeros(4, **i32)}
+    if ws is None:
+        ws = torch.empty(max(moe_permute_workspace_bytes(dm), 16), dtype=torch.uint8, device=dev)
+    _check(lib().moe_route_permute(ctypes.byref(dm), _ptr(logits), _ptr(out["ids"]),
+                                   _ptr(out["wts"]), _ptr(out["counts"]), _ptr(out["offsets"]),
+                                   _ptr(out["sorted_token"]), _ptr(out["row_of"]),
+                                   _ptr(out["tile_map"]), _ptr(out["num_tiles"]), _ptr(ws),
+                                   ws.numel(), _stream(stream)), "moe_route_permute")
     return out
 
 

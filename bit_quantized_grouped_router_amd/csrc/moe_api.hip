@@ -193,6 +193,28 @@ moe_status moe_permute(const moe_dims *dm, const int32_t *topk_ids, int32_t *cou
                                    tile_map, num_tiles, (int32_t *)ws, as_stream(stream)));
 }
 
+moe_status moe_route_permute(const moe_dims *dm, const float *logits, int32_t *topk_ids,
+                             float *topk_w, int32_t *counts, int32_t *offsets,
+                             int32_t *sorted_token, int32_t *row_of, int32_t *tile_map,
+                             int32_t *num_tiles, void *ws, size_t ws_bytes, void *stream) {
+  MOE_TRY(check_dims(dm));
+  if (dm->T == 0) return MOE_OK;
+  MOE_TRY(check_ptr(logits));
+  MOE_TRY(check_ptr(topk_ids));
+  MOE_TRY(check_ptr(topk_w));
+  MOE_TRY(check_ptr(counts));
+  MOE_TRY(check_ptr(offsets));
+  MOE_TRY(check_ptr(sorted_token));
+  MOE_TRY(check_ptr(row_of));
+  MOE_TRY(check_ptr(tile_map));
+  MOE_TRY(check_ptr(num_tiles));
+  MOE_TRY(check_ptr(ws));
+  if (ws_bytes < moe_permute_workspace_bytes(dm)) return MOE_E_WORKSPACE;
+  return hip_status(launch_route_permute(to_dims(dm), logits, topk_ids, topk_w, counts, offsets,
+                                         sorted_token, row_of, tile_map, num_tiles,
+                                         (int32_t *)ws, as_stream(stream)));
+}
+
 moe_status moe_expert_gate_up_w4(const moe_dims *dm, const uint16_t *x, const moe_w4_weights *w,
                                  const int32_t *sorted_token, const int32_t *tile_map,
                                  const int32_t *num_tiles, uint16_t *h, void *stream) {
@@ -255,9 +277,9 @@ static moe_status enqueue_layer(const Dims &d, const uint16_t *x, const float *l
                          float *y, const LayerWs &L, hipStream_t s) {
   if (decode_supported(d))
     return hip_status(launch_decode(d, x, logits, W, L.ids, L.wts, L.h, y, s));
-  MOE_TRY(hip_status(launch_route(logits, d.T, d.E, d.k, L.ids, L.wts, s)));
-  MOE_TRY(hip_status(launch_permute(d, L.ids, L.counts, L.offsets, L.sorted_token, L.row_of,
-                                    L.tile_map, L.num_tiles, L.block_counts, s)));
+  MOE_TRY(hip_status(launch_route_permute(d, logits, L.ids, L.wts, L.counts, L.offsets,
+                                          L.sorted_token, L.row_of, L.tile_map, L.num_tiles,
+                                          L.block_counts, s)));
   MOE_TRY(hip_status(launch_gate_up(d, x, W, L.sorted_token, L.tile_map, L.num_tiles, L.h, s)));
   MOE_TRY(hip_status(launch_down(d, L.h, W, L.tile_map, L.num_tiles, L.o_routed, L.o_shared, s)));
   return hip_status(launch_combine(d, L.o_routed, L.o_shared, L.wts, L.row_of, y, s));

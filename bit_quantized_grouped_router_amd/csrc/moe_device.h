@@ -226,17 +226,24 @@ __device__ __forceinline__ float group_sum(float v) {
 // expert (slot j in lane j, keys descending, equal keys by ascending index)
 // and its logit. If fewer than k keys exist (k > E cannot happen), ids stay
 // in [0, E).
+// This lane's logits of one token: experts lane, lane + 64, ... All loads are
+// unconditional (clamped index) so they are in flight together.
 template <int kMaxPerLane>
-__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int k,
-                                          int *out_id, float *out_logit) {
+__device__ __forceinline__ void wave_load_logits(const float *__restrict__ row, int E,
+                                                 float (&v)[kMaxPerLane]) {
   const int lane = threadIdx.x & (kWave - 1);
-  // all loads unconditional (clamped index) so they are in flight together
-  float v[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) {
     const int e = lane + i * kWave;
     v[i] = row[e < E ? e : 0];
   }
+}
+
+// The selection on logits already in registers (as wave_load_logits leaves them).
+template <int kMaxPerLane>
+__device__ __forceinline__ void wave_topk_loaded(const float (&v)[kMaxPerLane], int E, int k,
+                                                 int *out_id, float *out_logit) {
+  const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[kMaxPerLane];
 #pragma unroll
   for (int i = 0; i < kMaxPerLane; ++i) key[i] = lane + i * kWave < E ? logit_key(v[i]) : 0u;
@@ -277,6 +284,14 @@ __device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, 
   }
   *out_id = my_id;
   *out_logit = my_logit;
+}
+
+template <int kMaxPerLane>
+__device__ __forceinline__ void wave_topk(const float *__restrict__ row, int E, int k,
+                                          int *out_id, float *out_logit) {
+  float v[kMaxPerLane];
+  wave_load_logits<kMaxPerLane>(row, E, v);
+  wave_topk_loaded<kMaxPerLane>(v, E, k, out_id, out_logit);
 }
 
 }  // namespace moe

@@ -48,6 +48,12 @@ hipError_t launch_permute(const Dims &dm, const int32_t *ids, int32_t *counts, i
                           int32_t *sorted_token, int32_t *row_of, int32_t *tile_map,
                           int32_t *num_tiles, int32_t *block_counts, hipStream_t s);
 
+// moe_route then moe_permute; up to 64 tokens in one single-workgroup launch.
+hipError_t launch_route_permute(const Dims &dm, const float *logits, int32_t *ids, float *wts,
+                                int32_t *counts, int32_t *offsets, int32_t *sorted_token,
+                                int32_t *row_of, int32_t *tile_map, int32_t *num_tiles,
+                                int32_t *block_counts, hipStream_t s);
+
 hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
                           const int32_t *sorted_token, const int32_t *tile_map,
                           const int32_t *num_tiles, uint16_t *h, hipStream_t s);

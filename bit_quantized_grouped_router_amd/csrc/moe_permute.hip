@@ -255,6 +255,104 @@ __global__ __launch_bounds__(kPlaceThreads) void perm_place_kernel(
   }
 }
 
+// ------------------------------------------------------------------ small batches
+// Up to kSmallT tokens, routing and permutation take one workgroup and one
+// launch: wavefront w selects the top-k of tokens w, w + 16, w + 32 and
+// w + 48 (all their logits loaded before the first selection), the
+// histogram is counted in LDS, then the scan, tile map and schedule and the
+// stable scatter follow as in the two-kernel path (all tokens form a single
+// token block). Same outputs, bit for bit, as moe_route then moe_permute.
+constexpr int kSmallT = 64;
+constexpr int kSmallPerWave = kSmallT / (kPlaceThreads / kWave);  // 4
+
+template <int kMaxPerLane>
+__global__ __launch_bounds__(kPlaceThreads) void route_permute_small_kernel(
+    const float *__restrict__ logits, int T, int E, int k, int32_t *__restrict__ ids_out,
+    float *__restrict__ wts_out, int32_t *__restrict__ counts, int32_t *__restrict__ offsets,
+    int32_t *__restrict__ sorted_token, int32_t *__restrict__ row_of,
+    int32_t *__restrict__ tile_map, int32_t *__restrict__ num_tiles) {
+  __shared__ PlaceLds L;
+  __shared__ int cnt[kMaxExperts];
+  __shared__ int ids_s[kSmallT * 32];
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  for (int i = tid; i < E; i += kPlaceThreads) cnt[i] = 0;
+  float v[kSmallPerWave][kMaxPerLane];
+#pragma unroll
+  for (int i = 0; i < kSmallPerWave; ++i) {
+    const int t = wave + 16 * i;
+    wave_load_logits<kMaxPerLane>(logits + (size_t)(t < T ? t : T - 1) * E, E, v[i]);
+  }
+  __syncthreads();
+  // ---- top-k and router weights (the same arithmetic as the route kernel)
+#pragma unroll
+  for (int i = 0; i < kSmallPerWave; ++i) {
+    const int t = wave + 16 * i;
+    if (t >= T) break;  // wave-uniform
+    int id;
+    float l;
+    wave_topk_loaded<kMaxPerLane>(v[i], E, k, &id, &l);
+    const float m = __shfl(l, 0, kWave);
+    const float e = lane < k ? expf(l - m) : 0.f;
+    const float sum = wave_sum(e);
+    if (lane < k) {
+      ids_out[(size_t)t * k + lane] = id;
+      wts_out[(size_t)t * k + lane] = e / sum;
+      ids_s[t * k + lane] = id;
+      atomicAdd(&cnt[id], 1);
+    }
+  }
+  __syncthreads();
+  // ---- counts, offsets, tile map and schedule (thread e owns expert e)
+  const int c = tid < E ? cnt[tid] : 0;
+  const int c_incl = block_inclusive_scan(c, L.wave_tot);
+  write_tile_map(L, c, c_incl, T, E, k, counts, offsets, tile_map, num_tiles);
+  __syncthreads();  // the LDS union passes from the tile map to the scatter
+  // ---- stable scatter of the T*k assignments
+  if (tid < E) L.u.s.off[tid] = c_incl - c;
+  for (int i = tid; i < E * kMaskWords; i += kPlaceThreads) L.u.s.mask[i] = 0u;
+  __syncthreads();
+  const int TK = T * k;
+  for (int a = tid; a < TK; a += kPlaceThreads) {
+    const int t = a / k;
+    atomicOr(&L.u.s.mask[ids_s[a] * kMaskWords + (t >> 5)], 1u << (t & 31));
+  }
+  __syncthreads();
+  for (int a = tid; a < TK; a += kPlaceThreads) {
+    const int t = a / k, ex = ids_s[a];
+    const uint32_t *m = L.u.s.mask + ex * kMaskWords;
+    int rank = __popc(m[t >> 5] & ((1u << (t & 31)) - 1u));
+    for (int w = 0; w < (t >> 5); ++w) rank += __popc(m[w]);
+    const int p = L.u.s.off[ex] + rank;
+    sorted_token[p] = t;
+    row_of[a] = p;
+  }
+}
+
+hipError_t launch_route_permute(const Dims &dm, const float *logits, int32_t *ids, float *wts,
+                                int32_t *counts, int32_t *offsets, int32_t *sorted_token,
+                                int32_t *row_of, int32_t *tile_map, int32_t *num_tiles,
+                                int32_t *block_counts, hipStream_t s) {
+  if (dm.T > kSmallT) {
+    if (const hipError_t e = launch_route(logits, dm.T, dm.E, dm.k, ids, wts, s)) return e;
+    return launch_permute(dm, ids, counts, offsets, sorted_token, row_of, tile_map, num_tiles,
+                          block_counts, s);
+  }
+  if (dm.E <= 64)
+    route_permute_small_kernel<1><<<1, kPlaceThreads, 0, s>>>(
+        logits, dm.T, dm.E, dm.k, ids, wts, counts, offsets, sorted_token, row_of, tile_map,
+        num_tiles);
+  else if (dm.E <= 256)
+    route_permute_small_kernel<4><<<1, kPlaceThreads, 0, s>>>(
+        logits, dm.T, dm.E, dm.k, ids, wts, counts, offsets, sorted_token, row_of, tile_map,
+        num_tiles);
+  else
+    route_permute_small_kernel<16><<<1, kPlaceThreads, 0, s>>>(
+        logits, dm.T, dm.E, dm.k, ids, wts, counts, offsets, sorted_token, row_of, tile_map,
+        num_tiles);
+  return hipGetLastError();
+}
+
 hipError_t launch_permute(const Dims &dm, const int32_t *ids, int32_t *counts, int32_t *offsets,
                           int32_t *sorted_token, int32_t *row_of, int32_t *tile_map,
                           int32_t *num_tiles, int32_t *block_counts, hipStream_t s) {

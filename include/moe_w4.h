@@ -164,6 +164,21 @@ moe_status moe_permute(const moe_dims *dm, const int32_t *topk_ids, int32_t *cou
                        void *stream);
 
 /*
+ * moe_route_permute - moe_route followed by moe_permute, with the same
+ * outputs bit for bit. Up to 64 tokens it is a single one-workgroup launch
+ * (top-k, histogram, scan, block map and scatter together), which removes
+ * most of the fixed cost of the routing at small batches.
+ *   logits                      fp32 [T][E]
+ *   topk_ids, topk_w            out, as moe_route
+ *   counts .. num_tiles         out, as moe_permute
+ *   ws, ws_bytes                as moe_permute
+ */
+moe_status moe_route_permute(const moe_dims *dm, const float *logits, int32_t *topk_ids,
+                             float *topk_w, int32_t *counts, int32_t *offsets,
+                             int32_t *sorted_token, int32_t *row_of, int32_t *tile_map,
+                             int32_t *num_tiles, void *ws, size_t ws_bytes, void *stream);
+
+/*
  * moe_expert_gate_up_w4 - grouped gate/up GEMM over the block map with the
  * int4-g64 dequantisation fused into the tile (bf16 MFMA operands rebuilt in
  * LDS one K-tile at a time, fp32 accumulation; page section "Prefill e

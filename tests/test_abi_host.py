@@ -145,6 +145,18 @@ def test_permute_and_ffn_validation(L):
     assert L.moe_dequant_w4(None, 4, 128, FAKE, None) == INVALID
 
 
+def test_route_permute_validation(L):
+    rp = L.moe_route_permute
+    dm = _dims(T=300, d=256, f=128, E=16, k=4)
+    need = L.moe_permute_workspace_bytes(ctypes.byref(dm))
+    args = [FAKE] * 9
+    assert rp(ctypes.byref(_dims(T=0)), *([None] * 10), 0, None) == OK
+    assert rp(ctypes.byref(dm), None, *args[1:], FAKE, need, None) == INVALID
+    assert rp(ctypes.byref(dm), *args[:4], FAKE + 4, *args[5:], FAKE, need, None) == ALIGN
+    assert rp(ctypes.byref(dm), *args, FAKE, need - 4, None) == WORKSPACE
+    assert rp(ctypes.byref(_dims(k=9)), *args, FAKE, need, None) == INVALID
+
+
 def test_router_validation(L):
     r = L.moe_router_logits
     assert r(None, None, 0, 64, 8, None, None) == OK                   # T == 0: no-op

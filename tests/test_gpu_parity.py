@@ -95,6 +95,54 @@ def test_route_permute_bit_exact(cfg):
     assert np.array_equal(p["tile_map"][:n, 3], expected_schedule(ref["tiles"]))
 
 
+ROUTE_PERMUTE = [
+    G.small_config("rp_t1", T=1, d=64, f=64, E=256, k=8, seed=71),
+    G.small_config("rp_t2", T=2, d=64, f=64, E=256, k=8, seed=72),
+    G.small_config("rp_t37_e5", T=37, d=64, f=64, E=5, k=3, seed=73),
+    G.small_config("rp_t64_kE", T=64, d=64, f=64, E=8, k=8, seed=74),
+    G.small_config("rp_t64_e1000", T=64, d=64, f=64, E=1000, k=32, seed=75),
+    G.small_config("rp_t50_zipf_empty", T=50, d=64, f=64, E=256, k=8, seed=76, zipf_s=1.1,
+                   n_forced_empty=8),
+    G.small_config("rp_t65", T=65, d=64, f=64, E=256, k=8, seed=77),     # two-kernel path
+    G.small_config("rp_t300_zipf", T=300, d=64, f=64, E=64, k=4, seed=78, zipf_s=1.1),
+]
+
+
+@pytest.mark.parametrize("cfg", ROUTE_PERMUTE, ids=lambda c: c.name)
+def test_route_permute_one_call(cfg):
+    """moe_route_permute (one workgroup up to 64 tokens) against the oracle, bit for bit,
+    and against moe_route followed by moe_permute."""
+    say(f"[route_permute] {cfg.name}")
+    a = G.make_activations(cfg)
+    logits = torch.from_numpy(a["logits"]).cuda()
+    dm = M.dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
+    r = M.moe_route_permute(dm, logits)
+    ids, wts = M.moe_route(logits, cfg.k)
+    perm = M.moe_permute(dm, ids)
+    torch.cuda.synchronize()
+    p = {k: v.cpu().numpy() for k, v in r.items()}
+    rid, rw = O.route(a["logits"], cfg.k)
+    counts = O.histogram(rid, cfg.E)
+    offsets = O.exclusive_scan(counts)
+    st, row_of = O.scatter(rid, offsets)
+    tiles = O.block_map(counts, offsets, cfg.T, cfg.k, M.moe_block_m())
+    assert np.array_equal(p["ids"], rid)
+    assert np.abs(p["wts"] - rw).max() <= W_ABS
+    assert np.array_equal(p["counts"], counts)
+    assert np.array_equal(p["offsets"], offsets)
+    assert np.array_equal(p["sorted_token"][:cfg.T * cfg.k], st)
+    assert np.array_equal(p["row_of"][:cfg.T * cfg.k], row_of)
+    n = int(p["num_tiles"][0])
+    assert n == len(tiles)
+    assert np.array_equal(p["tile_map"][:n, :3], tiles)
+    assert np.array_equal(p["tile_map"][:n, 3], expected_schedule(tiles))
+    # the same bits as the two entry points
+    assert torch.equal(r["ids"], ids) and torch.equal(r["wts"], wts)
+    for key in ("counts", "offsets", "sorted_token", "row_of"):
+        assert torch.equal(r[key], perm[key]), key
+    assert torch.equal(r["tile_map"][:n], perm["tile_map"][:n])
+
+
 def _h_slack(cfg, inp, ref):
     T, k = cfg.T, cfg.k
     x = O.bf16_to_f64(inp["x"])
