@@ -11,7 +11,9 @@ step, inputs resident in HBM. Also reported on the same JSON line:
   decode        batch-1 decode: 1000 steps through the T=1 path, 32 weight
                 copies rotated so no step re-reads weights from cache, replayed
                 as a HIP graph; algorithmic bytes / time per step;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload.
+  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  small_batch   (--small-batch) the layer at T = 1 .. 64, bytes of the used
+                experts' weights / time.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 import argparse
@@ -73,6 +75,9 @@ def main():
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--small-batch", action="store_true",
+                    help="also time moe_layer_forward at T = 1, 2, 8, 32, 64 (off by default so the "
+                         "grouped GEMMs' profiled means stay those of the T=4096 launch)")
     ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (a reference "
@@ -209,6 +214,40 @@ def main():
                 "traffic": traffic_from_profile(GEMM_SOURCES, "gate_up_prefill_t4096_zipf"),
                 "algorithmic_flop_per_launch": flop_gate_up}
 
+    # ---------------------------------------------------------------- small batches
+    # moe_layer_forward at T = 1 .. 64 (the general path; T = 1 takes the
+    # decode kernels), two weight copies alternated, events around 100 calls
+    small = None
+    if args.small_batch:
+        log("[bench] small batches")
+        w2 = M.W4Weights.from_numpy(inp["weights"], device=dev)
+        wcs = [wc, w2.c()]
+        small = {}
+        for Ts in (1, 2, 8, 32, 64):
+            sc = G.small_config(f"small_t{Ts}", T=Ts, d=d, f=f, E=E, k=k, seed=7)
+            sa = G.make_activations(sc)
+            xs = torch.from_numpy(sa["x"].view(np.int16)).to(dev)
+            ls = torch.from_numpy(sa["logits"]).to(dev)
+            dms = M.dims(Ts, d, f, E, k)
+            wss = torch.empty(M.moe_layer_workspace_bytes(dms), dtype=torch.uint8, device=dev)
+            ys = torch.empty((Ts, d), dtype=torch.float32, device=dev)
+            ne = len(np.unique(M.moe_route(ls, k)[0].cpu().numpy()))
+            for i in range(10):
+                M.moe_layer_forward(dms, xs, ls, w, y=ys, ws=wss, wc=wcs[i % 2])
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for i in range(100):
+                M.moe_layer_forward(dms, xs, ls, w, y=ys, ws=wss, wc=wcs[i % 2])
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 10.0
+            by = (ne + 1) * expert_bytes(d, f) + Ts * (d * 2 + E * 4 + d * 4)
+            small[f"T={Ts}"] = {"us": round(us, 2), "experts": ne, "bytes": by,
+                                "GB/s": round(by / us / 1e3, 1),
+                                "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBPS, 4)}
+        del w2
+        log(f"[bench] small batches: {small}")
+
     # ---------------------------------------------------------------- decode
     decode = None
     if not args.no_decode:
@@ -326,6 +365,7 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "decode": decode,
+        "small_batch": small,
         "cpu_baseline": cpu,
     }
     print(json.dumps(out), flush=True)

@@ -33,7 +33,7 @@ page is silent, the readings taken here are:
   R7  o and y are kept unrounded (fp64 here);
   R8  block map: per group, ceil(count/BM) tiles of at most BM rows, groups in
       order 0..E-1 then the shared group E.
-  R9  router projection (the step before routing, for callers that start
+  R13 router projection (the step before routing, for callers that start
       from hidden states): the router's score of expert e for token t is the
       dot product of the token's bf16 hidden state with row e of a bf16
       matrix Wr [E, d]; the page says only that the router scores the 256
@@ -271,11 +271,11 @@ def combine(o: np.ndarray, w: np.ndarray, row_of: np.ndarray, T: int, k: int) ->
 
 
 # --------------------------------------------------------------------------
-# router projection (R9)
+# router projection (R13)
 # --------------------------------------------------------------------------
 
 def router_logits(x_bits: np.ndarray, wr_bits: np.ndarray) -> np.ndarray:
-    """R9: logits[t, e] = sum over c of x[t, c] * Wr[e, c], in fp64 over the
+    """R13: logits[t, e] = sum over c of x[t, c] * Wr[e, c], in fp64 over the
     exactly decoded bf16 values (section "O modelo em três formatos de carga":
     the router scores every expert for every token). x is [T, d], Wr is [E, d];
     the result is [T, E]."""

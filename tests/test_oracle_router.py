@@ -1,4 +1,4 @@
-"""Pins of the oracle's router projection (reading R9: logits = x . Wr^T over
+"""Pins of the oracle's router projection (reading R13: logits = x . Wr^T over
 bf16 values). Each pin is fixed by something other than the oracle's own
 formula: brute-force exact sums, unit rows that must copy one input column,
 and closed forms of all-ones inputs and exact scalings."""
