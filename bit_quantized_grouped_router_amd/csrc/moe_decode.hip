@@ -119,7 +119,7 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
       acc[r] = dot32_any(c[r], (uint32_t)sr[r] | ((uint32_t)br[r] << 16), xv, acc[r]);
   }
 #pragma unroll
-  for (int r = 0; r < 4; ++r) acc[r] = wave_sum(acc[r]);
+  for (int r = 0; r < 4; ++r) acc[r] = wave_sum_dpp(acc[r]);
   if (lane == 0) {
     h[(size_t)slot * f + n] = to_bf16(silu_mul(acc[0], acc[2]));
     h[(size_t)slot * f + n + 1] = to_bf16(silu_mul(acc[1], acc[3]));

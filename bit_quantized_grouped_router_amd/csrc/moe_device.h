@@ -210,6 +210,39 @@ __device__ __forceinline__ float wave_sum(float v) {
   return v;
 }
 
+// v plus the value a DPP lane pattern brings in (lanes of rows outside
+// row_mask add 0).
+template <int CTRL, int ROW_MASK>
+__device__ __forceinline__ float dpp_add(float v) {
+  const int o = __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL, ROW_MASK, 0xf, false);
+  return v + __builtin_bit_cast(float, o);
+}
+
+// Sum over the wavefront with six DPP steps (no LDS traffic): pairs and
+// quads, half-row and row mirrors, then the row broadcasts carry each row's
+// total into the next; the sum ends in lane 63 and is returned to all lanes.
+__device__ __forceinline__ float wave_sum_dpp(float v) {
+  v = dpp_add<0xb1, 0xf>(v);   // quad_perm 1,0,3,2
+  v = dpp_add<0x4e, 0xf>(v);   // quad_perm 2,3,0,1
+  v = dpp_add<0x141, 0xf>(v);  // row_half_mirror
+  v = dpp_add<0x140, 0xf>(v);  // row_mirror
+  v = dpp_add<0x142, 0xa>(v);  // row_bcast:15
+  v = dpp_add<0x143, 0xc>(v);  // row_bcast:31
+  return __builtin_bit_cast(float, __builtin_amdgcn_readlane(__builtin_bit_cast(int, v), 63));
+}
+
+// Sum over aligned groups of L lanes, L = 2, 4, 8 or 16, with DPP: every lane
+// of a group ends with the group's sum.
+template <int L>
+__device__ __forceinline__ float group_sum_dpp(float v) {
+  static_assert(L == 2 || L == 4 || L == 8 || L == 16, "DPP groups of 2 to 16 lanes");
+  v = dpp_add<0xb1, 0xf>(v);                   // pairs
+  if constexpr (L >= 4) v = dpp_add<0x4e, 0xf>(v);   // quads
+  if constexpr (L >= 8) v = dpp_add<0x141, 0xf>(v);  // half rows
+  if constexpr (L >= 16) v = dpp_add<0x140, 0xf>(v); // rows
+  return v;
+}
+
 // Sum over aligned groups of `width` lanes (width a power of two <= 64).
 template <int width>
 __device__ __forceinline__ float group_sum(float v) {

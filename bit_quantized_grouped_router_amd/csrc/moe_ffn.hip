@@ -516,6 +516,7 @@ static hipError_t gemm_setup() {
 hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
                           const int32_t *sorted_token, const int32_t *tile_map,
                           const int32_t *num_tiles, uint16_t *h, hipStream_t s) {
+  if (gemv_supported(dm)) return launch_gate_up_gemv(dm, x, w, sorted_token, tile_map, num_tiles, h, s);
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.f + kWgCols / 2 - 1) / (kWgCols / 2);
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
@@ -528,6 +529,7 @@ hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
 hipError_t launch_down(const Dims &dm, const uint16_t *h, const Weights &w,
                        const int32_t *tile_map, const int32_t *num_tiles, uint16_t *o_routed,
                        float *o_shared, hipStream_t s) {
+  if (gemv_supported(dm)) return launch_down_gemv(dm, h, w, tile_map, num_tiles, o_routed, o_shared, s);
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.d + kWgCols - 1) / kWgCols;
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));

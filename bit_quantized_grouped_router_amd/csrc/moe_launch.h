@@ -54,6 +54,17 @@ hipError_t launch_route_permute(const Dims &dm, const float *logits, int32_t *id
                                 int32_t *row_of, int32_t *tile_map, int32_t *num_tiles,
                                 int32_t *block_counts, hipStream_t s);
 
+// Small batches: the same projections with a few weight rows per wavefront
+// and dot products on the VALU (launch_gate_up / launch_down call these when
+// gemv_supported).
+bool gemv_supported(const Dims &dm);
+hipError_t launch_gate_up_gemv(const Dims &dm, const uint16_t *x, const Weights &w,
+                               const int32_t *sorted_token, const int32_t *tile_map,
+                               const int32_t *num_tiles, uint16_t *h, hipStream_t s);
+hipError_t launch_down_gemv(const Dims &dm, const uint16_t *h, const Weights &w,
+                            const int32_t *tile_map, const int32_t *num_tiles,
+                            uint16_t *o_routed, float *o_shared, hipStream_t s);
+
 hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
                           const int32_t *sorted_token, const int32_t *tile_map,
                           const int32_t *num_tiles, uint16_t *h, hipStream_t s);

@@ -33,6 +33,13 @@ SMALL = [
     # K = 6144 leave room for one workgroup per CU)
     G.small_config("max_d6144_t40", T=40, d=6144, f=64, E=3, k=2, seed=18),
     G.small_config("max_f6144_t40", T=40, d=64, f=6144, E=3, k=2, seed=19),
+    # up to 6 tokens the expert projections run on the VALU kernels (a few
+    # weight rows per wavefront); f / 32 lanes per down row: 2, 4, 16, 32, 64
+    G.small_config("gemv_t3_f64", T=3, d=64, f=64, E=4, k=2, seed=20),
+    G.small_config("gemv_t5_d192", T=5, d=192, f=128, E=5, k=3, seed=21),
+    G.small_config("gemv_t6_full_width", T=6, d=2048, f=512, E=256, k=8, seed=22),
+    G.small_config("gemv_t6_f1024", T=6, d=512, f=1024, E=16, k=4, seed=24),
+    G.small_config("gemv_t4_f2048", T=4, d=256, f=2048, E=8, k=2, seed=23),
 ]
 
 
