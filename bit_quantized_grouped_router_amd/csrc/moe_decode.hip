@@ -206,7 +206,11 @@ __global__ __launch_bounds__(128) void decode_down_kernel(
     const uint4 hv[4] = {hp[0], hp[1], hp[2], hp[3]};
     part += dot32_any(csh, (uint32_t)ssh | ((uint32_t)bsh << 16), hv, 0.f);
   }
-  const float acc = group_sum<kLanesPerRow>(part);
+  float acc;
+  if constexpr (kLanesPerRow <= 16)
+    acc = group_sum_dpp<kLanesPerRow>(part);
+  else
+    acc = group_sum<kLanesPerRow>(part);
   if (lane % kLanesPerRow == 0) y[m] = acc;
 }
 
