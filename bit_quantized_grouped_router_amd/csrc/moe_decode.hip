@@ -54,16 +54,19 @@ __device__ __forceinline__ float dot32_any(uint4 c, uint32_t sb, const uint4 *xv
 // One wavefront = one slot (routed slot j < k, or the shared expert at
 // j == k) and two intermediate units (4 weight rows). Loads are issued as
 // early as their addresses are known: x first, the shared expert's rows at
-// once, a routed slot's rows right after its own on-chip top-k.
+// once, a routed slot's rows right after the workgroup's on-chip top-k.
 template <int kMaxPerLane>
 __global__ __launch_bounds__(256) void decode_gate_up_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, W4 w13, W4 s13, int d,
     int f, int E, int k, int32_t *__restrict__ ids_out, float *__restrict__ wts_out,
     uint16_t *__restrict__ h) {
+  __shared__ int s_expert;
   const int lane = threadIdx.x & 63;
-  const int gw = __builtin_amdgcn_readfirstlane(blockIdx.x * 4 + (threadIdx.x >> 6));
+  const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const int gw = blockIdx.x * 4 + wave;
+  // the launch has exactly (k + 1) * f / 2 wavefronts (f % 8 == 0), and the
+  // 8 units of a workgroup belong to one slot
   const int item = gw * kDecUnitsPerWave;
-  if (item >= (k + 1) * f) return;
   const int slot = item / f, n = item % f;
   const bool shared = slot == k;
   // this lane's first 32 columns of x, loaded before the routing (independent of it)
@@ -75,12 +78,13 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
     xv0[2] = xp[2];
     xv0[3] = xp[3];
   }
-  int expert = 0;
-  if (!shared || gw == 0) {
+  // the top-k once per workgroup (wavefront 0; the other three wait at the
+  // barrier instead of repeating it), shared through LDS
+  if (wave == 0 && !shared) {
     int id;
     float l;
     wave_topk<kMaxPerLane>(logits, E, k, &id, &l);
-    if (!shared) expert = __builtin_amdgcn_readlane(id, slot);
+    if (lane == slot) s_expert = id;
     if (gw == 0) {
       const float m = __shfl(l, 0, kWave);
       const float e = lane < k ? expf(l - m) : 0.f;
@@ -91,6 +95,8 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
       }
     }
   }
+  __syncthreads();
+  const int expert = shared ? 0 : __builtin_amdgcn_readfirstlane(s_expert);
   const W4 W = shared ? s13 : w13;
   const size_t rb = (size_t)expert * 2 * f;
   const size_t rows[4] = {rb + n, rb + n + 1, rb + f + n, rb + f + n + 1};
