@@ -303,10 +303,66 @@ __global__ __launch_bounds__(kPlaceThreads) void route_permute_small_kernel(
     }
   }
   __syncthreads();
-  // ---- counts, offsets, tile map and schedule (thread e owns expert e)
+  // ---- counts, offsets, tile map and schedule (thread e owns expert e).
+  // Fewer than kBlockM tokens: every non-empty group is a single partial
+  // tile, so one scan of (rows, 1 << 16 per tile) gives both the offsets and
+  // the tile indices, and the schedule only orders heights 1 .. T.
+  static_assert(kSmallT < kBlockM, "one partial tile per group");
+  for (int i = tid; i < (kSmallT + 1) * kGroupWords; i += kPlaceThreads) (&L.u.m.hmask[0][0])[i] = 0u;
   const int c = tid < E ? cnt[tid] : 0;
-  const int c_incl = block_inclusive_scan(c, L.wave_tot);
-  write_tile_map(L, c, c_incl, T, E, k, counts, offsets, tile_map, num_tiles);
+  const int packed = block_inclusive_scan(c + (c > 0 ? 1 << 16 : 0), L.wave_tot);
+  const int c_incl = packed & 0xFFFF, tiles_incl = packed >> 16;
+  const int tile_e = tiles_incl - (c > 0);
+  if (tid < E) {
+    counts[tid] = c;
+    offsets[tid] = c_incl - c;
+    if (c > 0) {
+      int32_t *row = tile_map + 4 * (size_t)tile_e;
+      row[0] = tid;
+      row[1] = c_incl - c;
+      row[2] = c_incl;
+      atomicOr(&L.u.m.hmask[c][tid >> 5], 1u << (tid & 31));
+    }
+  }
+  if (tid == kPlaceThreads - 1) {
+    offsets[E] = c_incl;  // == T*k
+    L.routed_tiles = tiles_incl;
+  }
+  if (tid == 0) atomicOr(&L.u.m.hmask[T][E >> 5], 1u << (E & 31));  // the shared group's tile
+  __syncthreads();
+  const int shared_tile = L.routed_tiles;
+  if (tid == 0) {
+    int32_t *row = tile_map + 4 * (size_t)shared_tile;
+    row[0] = E;
+    row[1] = T * k;
+    row[2] = T * k + T;
+    *num_tiles = shared_tile + 1;
+  }
+  // first schedule position of each height, tallest first: one wavefront,
+  // lane l for height kSmallT - l
+  if (tid < kWave) {
+    const int hgt = kSmallT - tid;
+    int hc = 0;
+    if (hgt >= 1)
+      for (int w = 0; w < kGroupWords; ++w) hc += __popc(L.u.m.hmask[hgt][w]);
+    int incl = hc;
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+      const int o = __shfl_up(incl, off, kWave);
+      if (tid >= off) incl += o;
+    }
+    if (hgt >= 1) L.u.m.hstart[hgt] = incl - hc;
+  }
+  __syncthreads();
+  // schedule entries: equal heights in group (= tile) order; group g's rank
+  // among its height's groups counts the bits below g
+  auto rank_of = [&](int g, int h) {
+    int rank = __popc(L.u.m.hmask[h][g >> 5] & ((1u << (g & 31)) - 1u));
+    for (int w = 0; w < (g >> 5); ++w) rank += __popc(L.u.m.hmask[h][w]);
+    return L.u.m.hstart[h] + rank;
+  };
+  if (tid < E && c > 0) tile_map[4 * (size_t)rank_of(tid, c) + 3] = tile_e;
+  if (tid == 0) tile_map[4 * (size_t)rank_of(E, T) + 3] = shared_tile;
   __syncthreads();  // the LDS union passes from the tile map to the scatter
   // ---- stable scatter of the T*k assignments
   if (tid < E) L.u.s.off[tid] = c_incl - c;
