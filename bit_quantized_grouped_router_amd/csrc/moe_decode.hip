@@ -61,6 +61,15 @@ __global__ __launch_bounds__(256) void decode_gate_up_kernel(
     int f, int E, int k, int32_t *__restrict__ ids_out, float *__restrict__ wts_out,
     uint16_t *__restrict__ h) {
   __shared__ int s_expert;
+  // token blockIdx.y (a few tokens take the same kernels, one grid row each)
+  {
+    const int t = blockIdx.y;
+    x += (size_t)t * d;
+    logits += (size_t)t * E;
+    ids_out += (size_t)t * k;
+    wts_out += (size_t)t * k;
+    h += (size_t)t * (k + 1) * f;
+  }
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * 4 + wave;
@@ -147,6 +156,13 @@ __global__ __launch_bounds__(128) void decode_down_kernel(
     const uint16_t *__restrict__ h, W4 w2, W4 s2, int d, int f, int E, int k,
     float *__restrict__ y) {
   extern __shared__ __attribute__((aligned(16))) uint16_t hs[];
+  {
+    const int t = blockIdx.y;  // token
+    ids += (size_t)t * k;
+    wts += (size_t)t * k;
+    h += (size_t)t * (k + 1) * f;
+    y += (size_t)t * d;
+  }
   const int tid = threadIdx.x;
   constexpr int kRowsPerWave = kWave / kLanesPerRow;
   const int wave = tid >> 6, lane = tid & 63;
@@ -220,10 +236,15 @@ __global__ __launch_bounds__(128) void decode_down_kernel(
   if (lane % kLanesPerRow == 0) y[m] = acc;
 }
 
+// Tokens up to which the layer runs these kernels, one grid row per token
+// (each token's experts are streamed for it alone; the weights two tokens
+// share come from the caches the second time).
+constexpr int kDecodeMaxT = 16;
+
 bool decode_supported(const Dims &dm) {
   const int lpr = dm.f / 32;
   const bool pow2 = lpr >= 2 && lpr <= 64 && (lpr & (lpr - 1)) == 0;
-  return dm.T == 1 && pow2 && (size_t)(dm.k + 1) * dm.f * 2 <= 48 * 1024 &&
+  return dm.T >= 1 && dm.T <= kDecodeMaxT && pow2 && (size_t)(dm.k + 1) * dm.f * 2 <= 48 * 1024 &&
          (size_t)h_stage_chunks(dm.k <= 8 ? 8 : 32, dm.f) * 128 * 16 <= 48 * 1024;
 }
 
@@ -240,10 +261,10 @@ static void launch_down_t(const Dims &dm, const int32_t *ids, const float *wts, 
     return need > staged ? need : staged;
   };
   if (dm.k <= 8)
-    decode_down_kernel<kLanesPerRow, 8><<<blocks, 128, lds_bytes(8), s>>>(
+    decode_down_kernel<kLanesPerRow, 8><<<dim3(blocks, dm.T), 128, lds_bytes(8), s>>>(
         ids, wts, h, w.w2, w.s2, dm.d, dm.f, dm.E, dm.k, y);
   else
-    decode_down_kernel<kLanesPerRow, 32><<<blocks, 128, lds_bytes(32), s>>>(
+    decode_down_kernel<kLanesPerRow, 32><<<dim3(blocks, dm.T), 128, lds_bytes(32), s>>>(
         ids, wts, h, w.w2, w.s2, dm.d, dm.f, dm.E, dm.k, y);
 }
 
@@ -252,13 +273,13 @@ hipError_t launch_decode(const Dims &dm, const uint16_t *x, const float *logits,
   const int waves = (dm.k + 1) * dm.f / kDecUnitsPerWave;
   const int blocks = (waves + 3) / 4;
   if (dm.E <= 64)
-    decode_gate_up_kernel<1><<<blocks, 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
+    decode_gate_up_kernel<1><<<dim3(blocks, dm.T), 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
                                                     dm.k, ids, wts, h);
   else if (dm.E <= 256)
-    decode_gate_up_kernel<4><<<blocks, 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
+    decode_gate_up_kernel<4><<<dim3(blocks, dm.T), 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
                                                     dm.k, ids, wts, h);
   else
-    decode_gate_up_kernel<16><<<blocks, 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
+    decode_gate_up_kernel<16><<<dim3(blocks, dm.T), 256, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
                                                      dm.k, ids, wts, h);
   switch (dm.f / 32) {
     case 2: launch_down_t<2>(dm, ids, wts, h, w, y, s); break;

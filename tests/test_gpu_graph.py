@@ -42,6 +42,7 @@ def _setup(cfg):
     G.small_config("graph_prefill_t300", T=300, d=256, f=128, E=16, k=4, seed=41, zipf_s=1.1),
     G.small_config("graph_prefill_t700", T=700, d=512, f=256, E=64, k=8, seed=42),
     G.small_config("graph_decode_t1", T=1, d=2048, f=512, E=256, k=8, seed=43),
+    G.small_config("graph_decode_t5", T=5, d=512, f=256, E=64, k=8, seed=44),
 ], ids=lambda c: c.name)
 def test_graph_replays_match_eager(cfg):
     say(f"[graph] {cfg.name}")

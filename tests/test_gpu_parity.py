@@ -19,6 +19,10 @@ from parity_util import (W_ABS, check_bf16_close, check_y, dev_bits, expected_sc
 
 pytestmark = pytest.mark.gpu
 
+# tokens up to which moe_layer_forward runs the per-token decode kernels
+# (one grid row per token) rather than the routed, permuted grouped path
+DECODE_MAX_T = 16
+
 SMALL = [
     G.CONFIGS["tiny_t16"],
     G.small_config("ragged_t37_d192", T=37, d=192, f=128, E=5, k=3, seed=11),
@@ -218,9 +222,13 @@ def test_layer_forward_matches_oracle(cfg):
     y = M.moe_layer_forward(dm, x, logits, w)
     torch.cuda.synchronize()
     check_y(y.cpu().numpy(), ref["y"])
-    if cfg.T >= 2:
+    if cfg.T > DECODE_MAX_T:
         # one call runs exactly the staged kernels: identical bits
         assert torch.equal(y, staged(cfg)["y"])
+    else:
+        # up to DECODE_MAX_T tokens the layer takes the per-token decode
+        # kernels instead; the staged path agrees within the same tolerance
+        check_y(staged(cfg)["y"].cpu().numpy(), ref["y"], "staged y")
 
 
 def test_dequant_bit_exact_exhaustive_scales():
