@@ -228,10 +228,13 @@ size_t moe_layer_workspace_bytes(const moe_dims *dm);
 
 /*
  * moe_layer_forward - the whole layer on one stream with no host sync:
- * route, permute, gate/up, down, combine (T >= 2), or the batch-1 decode
- * path (T == 1: routing recomputed on chip, the 9 experts' 4-bit weights
- * streamed with 128-bit loads; page section "Prefill e decode: onde estao os
- * ganhos": at batch 1 bandwidth sets the ceiling).
+ * route, permute, gate/up, down, combine, or, for up to 16 tokens, the
+ * decode path (two launches, one grid row per token: routing recomputed on
+ * chip, each token's 9 experts' 4-bit weights streamed with 128-bit loads;
+ * page section "Prefill e decode: onde estao os ganhos": at small batches
+ * bandwidth sets the ceiling). The two paths agree within rounding; the
+ * workspace's routing and permutation buffers are only written by the
+ * first.
  *   x      bf16 [T][d]
  *   logits fp32 [T][E]
  *   y      fp32 [T][d] out
@@ -244,7 +247,7 @@ moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float 
 /*
  * moe_layer_forward_hidden - moe_layer_forward starting from hidden states:
  * moe_router_logits into the workspace, then the layer on those logits (the
- * same kernels, T == 1 included). Every argument is validated before the
+ * same kernels, small batches included). Every argument is validated before the
  * first launch.
  *   x         bf16 [T][d]
  *   w_router  bf16 [E][d]
