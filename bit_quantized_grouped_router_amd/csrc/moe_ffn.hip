@@ -7,7 +7,8 @@
 //   - one workgroup = 4 wavefronts = a tile of <= 128 permuted rows (from the
 //     block map) x 256 weight rows; every wavefront covers all 128 rows and
 //     its own 64 weight rows, so each weight is dequantised exactly once per
-//     tile and 32-row slabs past the tile's last row skip their MFMAs;
+//     tile; 32-row blocks past the tile's last row are not moved, read or
+//     multiplied (the K loop is compiled for 1..4 active blocks);
 //   - v_mfma_f32_32x32x16_bf16 with fp32 accumulators (4 x 2 blocks of 32x32
 //     per wavefront);
 //   - the weights never pass through LDS: each lane loads 16 bytes of codes
@@ -82,12 +83,15 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // Activations of K step src into ring stage `stage`: this lane's 16-byte
 // chunks (see the kernel for the lane -> row/chunk assignment), LDS DMA
 // through a buffer resource (byte offsets: a_off, plus the step as a scalar).
+// DMA instruction i fills 32-row block i of the tile, so a tile with NRB
+// active row blocks issues the first NRB.
+template <int NRB>
 __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t actr,
                                           const uint32_t (&a_off)[kDma], uint8_t *lds,
                                           uint32_t a_lds, int src, int stage) {
   uint8_t *s = lds + stage * kStageBytes + a_lds;
 #pragma unroll
-  for (int i = 0; i < kDma; ++i)
+  for (int i = 0; i < NRB; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(actr, (lds_void *)(s + i * kDmaRows * 128), 16, a_off[i],
                                              src * (kKT * 2), 0, 0);
 }
@@ -107,17 +111,19 @@ struct TileSetup {
   int nrb;                // active 32-row blocks of the tile (1..kRB), wave-uniform
 };
 
-// K loop of one tile. FULL: all row blocks active (no per-block branches
-// inside the K step). FAST: every group of this wavefront's weight rows
-// takes the fast dequantisation.
+// K loop of one tile. NRB: the tile's active 32-row blocks (1..kRB), known
+// at compile time, so a short tile moves, reads and multiplies only the rows
+// it has (the activation DMA, the A-fragment reads and the MFMAs all scale
+// with NRB; the dequantisation does not). FAST: every group of this
+// wavefront's weight rows takes the fast dequantisation.
 //
 // Order of one K step kt: wait until this wavefront's DMA of stage kt has
-// landed (at most the four DMA chunks of stage kt+1, issued one step later,
+// landed (at most the NRB DMA chunks of stage kt+1, issued one step later,
 // may still be in flight; code loads issued after them only make the wait
 // stricter), barrier (every wavefront's stage kt is in LDS, and every
 // wavefront is done with stage kt-1), DMA of stage kt+2 into the slot of
 // stage kt-1, code loads for step kt+2, then the four K slices.
-template <bool FULL, bool FAST>
+template <int NRB, bool FAST>
 __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
                                             f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
                                             const u32x4_t (&cr1)[2]) {
@@ -141,7 +147,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   // stay in the instruction stream (so every wait count holds) but touch no
   // memory and return zeros into a stage or code slot no one reads
 #define MOE_DMA(src_, stage_)                                                                \
-  dma_stage((src_) <= klast ? st.actr : st.actr_none, st.a_off, lds, st.a_lds,               \
+  dma_stage<NRB>((src_) <= klast ? st.actr : st.actr_none, st.a_off, lds, st.a_lds,          \
             (src_) <= klast ? (src_) : 0, (stage_))
 #define MOE_LOAD_B(kt_, slot_)                                                              \
   {                                                                                         \
@@ -177,7 +183,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
 #define MOE_STEP(kt_, slot_)                                                                 \
   {                                                                                          \
     const int ktv_ = (kt_);                                                                  \
-    MOE_WAIT_VMCNT(kDma + 2);                                                                \
+    MOE_WAIT_VMCNT(NRB + 2);                                                                 \
     __builtin_amdgcn_s_barrier();                                                            \
     /* no LDS access or use of this step's codes moves above the wait and barrier */        \
     asm volatile("" : "+v"(cr[slot_][0]), "+v"(cr[slot_][1])::"memory");                    \
@@ -193,8 +199,8 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
     const DqGroup q0_ = dq_consts(s0_), q1_ = dq_consts(s1_);                                \
     _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                       \
       const uint8_t *aks_ = abuf_ + lrow + (((lh + ks) ^ lx) << 4);                          \
-      bf16x8_t a_[kRB];                                                                      \
-      _Pragma("unroll") for (int rb = 0; rb < kRB; ++rb)                                     \
+      bf16x8_t a_[NRB];                                                                      \
+      _Pragma("unroll") for (int rb = 0; rb < NRB; ++rb)                                     \
         a_[rb] = __builtin_bit_cast(bf16x8_t, *(const uint4 *)(aks_ + rb * 4096));           \
       bf16x8_t n0_, n1_;                                                                     \
       if (ks < 3) {                                                                          \
@@ -204,8 +210,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
         MOE_DQ(cr[((slot_) + 1) % 3][0][0], cr[((slot_) + 1) % 3][1][0], r0_, r1_, sb0, sb1, \
                n0_, n1_);                                                                    \
       }                                                                                      \
-      _Pragma("unroll") for (int rb = 0; rb < kRB; ++rb) {                                   \
-        if (!FULL && rb >= st.nrb) continue;                                                 \
+      _Pragma("unroll") for (int rb = 0; rb < NRB; ++rb) {                                   \
         acc[rb][0] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[rb], bq0, acc[rb][0], 0, 0, 0); \
         acc[rb][1] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a_[rb], bq1, acc[rb][1], 0, 0, 0); \
       }                                                                                      \
@@ -239,6 +244,27 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
 #undef MOE_DQ
 #undef MOE_DMA
 #undef MOE_LOAD_B
+}
+
+// DMA of ring stages 0 and 1 (K steps 0 and 1) for a tile of NRB row blocks.
+template <int NRB>
+__device__ __forceinline__ void prologue_dma(const TileSetup &st, uint8_t *lds, int klast) {
+  dma_stage<NRB>(st.actr, st.a_off, lds, st.a_lds, 0, 0);
+  dma_stage<NRB>(st.actr, st.a_off, lds, st.a_lds, min(1, klast), 1);
+}
+
+// The K loop for a tile of NRB row blocks, entered once stage 0 has landed
+// (only the NRB chunks of stage 1 may still be in flight, so the loop's
+// first wait holds at once).
+template <int NRB>
+__device__ __forceinline__ void tile_k_loop(const TileSetup &st, uint8_t *lds,
+                                            f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
+                                            const u32x4_t (&cr1)[2], bool fast) {
+  MOE_WAIT_VMCNT(NRB);
+  if (fast)
+    gemm_k_loop<NRB, true>(st, lds, acc, cr0, cr1);
+  else
+    gemm_k_loop<NRB, false>(st, lds, acc, cr0, cr1);
 }
 
 template <int KIND>
@@ -360,8 +386,16 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
       st.a_off[i] = ((uint32_t)t * (uint32_t)K + j * 8u) * 2u;  // token clamped: in range for any routing
     }
   }
-  dma_stage(st.actr, st.a_off, smem, st.a_lds, 0, 0);
-  dma_stage(st.actr, st.a_off, smem, st.a_lds, min(1, klast), 1);
+  // the tile's active 32-row blocks (the same for every wavefront: the DMA
+  // fills each row block with all four), clamped to 1..kRB for any map
+  const int rows = row_end - row_begin;
+  const int tile_rb = min(max((rows + 31) / 32, 1), kRB);
+  switch (tile_rb) {
+    case 1: prologue_dma<1>(st, smem, klast); break;
+    case 2: prologue_dma<2>(st, smem, klast); break;
+    case 3: prologue_dma<3>(st, smem, klast); break;
+    default: prologue_dma<kRB>(st, smem, klast); break;
+  }
   if (vec) {
     for (int g0 = 0; g0 < ng; g0 += 32) {
       if (g0 > 0) {
@@ -395,25 +429,18 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
     }
   }
   const bool fast = __builtin_amdgcn_ballot_w64(!fast_ok) == 0;  // wave-uniform
-  const int rows = row_end - row_begin;
-  st.nrb = wave_on ? (rows + 31) / 32 : 0;
+  st.nrb = wave_on ? tile_rb : 0;
 
   f32x16_t acc[kRB][2];
 #pragma unroll
   for (int rb = 0; rb < kRB; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
-  // stage 0 has landed (only the four chunks of stage 1 may still be in
-  // flight); the loop's first wait then holds at once
-  MOE_WAIT_VMCNT(kDma);
-  if (st.nrb == kRB) {
-    if (fast)
-      gemm_k_loop<true, true>(st, smem, acc, cr0, cr1);
-    else
-      gemm_k_loop<true, false>(st, smem, acc, cr0, cr1);
-  } else {
-    if (fast)
-      gemm_k_loop<false, true>(st, smem, acc, cr0, cr1);
-    else
-      gemm_k_loop<false, false>(st, smem, acc, cr0, cr1);
+  // a wavefront with no weight rows runs the same loop (its share of the
+  // DMA and the barriers are needed) and stores nothing
+  switch (tile_rb) {
+    case 1: tile_k_loop<1>(st, smem, acc, cr0, cr1, fast); break;
+    case 2: tile_k_loop<2>(st, smem, acc, cr0, cr1, fast); break;
+    case 3: tile_k_loop<3>(st, smem, acc, cr0, cr1, fast); break;
+    default: tile_k_loop<kRB>(st, smem, acc, cr0, cr1, fast); break;
   }
 
   // ---- epilogue. Every wavefront is past its last LDS read of the ring
