@@ -44,6 +44,10 @@ SMALL = [
     G.small_config("gemv_t6_full_width", T=6, d=2048, f=512, E=256, k=8, seed=22),
     G.small_config("gemv_t6_f1024", T=6, d=512, f=1024, E=16, k=4, seed=24),
     G.small_config("gemv_t4_f2048", T=4, d=256, f=2048, E=8, k=2, seed=23),
+    # decode kernels with more slots than the down kernel's 16 wavefronts
+    # (wavefronts take two or three slots each), and f / 32 = 8 lanes per row
+    G.small_config("decode_k20_f256", T=3, d=128, f=256, E=40, k=20, seed=25),
+    G.small_config("decode_k32_t16", T=16, d=64, f=64, E=64, k=32, seed=26),
 ]
 
 
