@@ -32,12 +32,11 @@ __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
   return acc;
 }
 
-// intermediate units per wavefront and wavefronts per workgroup of
-// decode_gate_up: the workgroup's 4 units belong to one slot (f % 64 == 0).
-// One unit (a gate row and an up row) per wavefront keeps every SIMD busy
-// with the dequantisation once the weights arrive.
-constexpr int kDecUnitsPerWave = 1;
+// wavefronts per workgroup of decode_gate_up; the workgroup's units (4 or 8)
+// belong to one slot (f % 64 == 0)
 constexpr int kDecWaves = 4;
+// tokens up to which decode_gate_up takes one unit per wavefront (two above)
+constexpr int kDecOneUnitMaxT = 4;
 // wavefronts of a decode_down_slots workgroup at most (one per expert slot)
 constexpr int kDownSlotWaves = 16;
 
@@ -57,7 +56,8 @@ __device__ __forceinline__ float dot32_any(uint4 c, uint32_t sb, const uint4 *xv
 // j == k) and two intermediate units (4 weight rows). Loads are issued as
 // early as their addresses are known: x first, the shared expert's rows at
 // once, a routed slot's rows right after the workgroup's on-chip top-k.
-template <int kMaxPerLane>
+// U intermediate units (a gate row and an up row each) per wavefront.
+template <int kMaxPerLane, int U>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, W4 w13, W4 s13, int d,
     int f, int E, int k, int32_t *__restrict__ ids_out, float *__restrict__ wts_out,
@@ -75,9 +75,9 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   const int lane = threadIdx.x & 63;
   const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const int gw = blockIdx.x * kDecWaves + wave;
-  // the launch has exactly (k + 1) * f / kDecUnitsPerWave wavefronts, and the
-  // kDecUnitsPerWave * kDecWaves (<= 8) units of a workgroup belong to one slot
-  const int item = gw * kDecUnitsPerWave;
+  // the launch has exactly (k + 1) * f / U wavefronts, and the U * kDecWaves
+  // (<= 8) units of a workgroup belong to one slot
+  const int item = gw * U;
   const int slot = item / f, n = item % f;
   const bool shared = slot == k;
   // this lane's first 32 columns of x, loaded before the routing (independent of it)
@@ -111,7 +111,6 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   const W4 W = shared ? s13 : w13;
   const size_t rb = (size_t)expert * 2 * f;
   // gate rows n .. n + U - 1, then the up rows f + n ..
-  constexpr int U = kDecUnitsPerWave;
   size_t rows[2 * U];
 #pragma unroll
   for (int u = 0; u < U; ++u) {
@@ -222,24 +221,40 @@ template <int kLanesPerRow>
 static void launch_down_slots(const Dims &dm, const int32_t *ids, const float *wts,
                               const uint16_t *h, const Weights &w, float *y, hipStream_t s) {
   constexpr int R = kWave / kLanesPerRow;
-  const int waves = dm.k + 1 < kDownSlotWaves ? dm.k + 1 : kDownSlotWaves;
+  // every slot its own wavefront at one token; with more tokens (grid rows)
+  // each wavefront takes several slots
+  const int per = dm.T <= 1 ? 1 : (dm.T <= 2 ? 2 : (dm.T <= 4 ? 4 : (dm.T <= 8 ? 5 : 9)));
+  int waves = (dm.k + per) / per;
+  if (waves > kDownSlotWaves) waves = kDownSlotWaves;
   decode_down_slots_kernel<kLanesPerRow><<<dim3(dm.d / R, dm.T), waves * kWave, 0, s>>>(
       ids, wts, h, w.w2, w.s2, dm.d, dm.f, dm.E, dm.k, y);
 }
 
+template <int kMaxPerLane, int U>
+static void launch_gate_up_t(const Dims &dm, const uint16_t *x, const float *logits,
+                             const Weights &w, int32_t *ids, float *wts, uint16_t *h, hipStream_t s) {
+  const int blocks = (dm.k + 1) * dm.f / U / kDecWaves;  // f % 64 == 0: whole workgroups
+  decode_gate_up_kernel<kMaxPerLane, U><<<dim3(blocks, dm.T), kDecWaves * 64, 0, s>>>(
+      x, logits, w.w13, w.s13, dm.d, dm.f, dm.E, dm.k, ids, wts, h);
+}
+
 hipError_t launch_decode(const Dims &dm, const uint16_t *x, const float *logits, const Weights &w,
                          int32_t *ids, float *wts, uint16_t *h, float *y, hipStream_t s) {
-  const int waves = (dm.k + 1) * dm.f / kDecUnitsPerWave;
-  const int blocks = waves / kDecWaves;  // f % 8 == 0: whole workgroups
-  if (dm.E <= 64)
-    decode_gate_up_kernel<1><<<dim3(blocks, dm.T), kDecWaves * 64, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
-                                                    dm.k, ids, wts, h);
-  else if (dm.E <= 256)
-    decode_gate_up_kernel<4><<<dim3(blocks, dm.T), kDecWaves * 64, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
-                                                    dm.k, ids, wts, h);
-  else
-    decode_gate_up_kernel<16><<<dim3(blocks, dm.T), kDecWaves * 64, 0, s>>>(x, logits, w.w13, w.s13, dm.d, dm.f, dm.E,
-                                                     dm.k, ids, wts, h);
+  if (dm.T <= kDecOneUnitMaxT) {
+    if (dm.E <= 64)
+      launch_gate_up_t<1, 1>(dm, x, logits, w, ids, wts, h, s);
+    else if (dm.E <= 256)
+      launch_gate_up_t<4, 1>(dm, x, logits, w, ids, wts, h, s);
+    else
+      launch_gate_up_t<16, 1>(dm, x, logits, w, ids, wts, h, s);
+  } else {
+    if (dm.E <= 64)
+      launch_gate_up_t<1, 2>(dm, x, logits, w, ids, wts, h, s);
+    else if (dm.E <= 256)
+      launch_gate_up_t<4, 2>(dm, x, logits, w, ids, wts, h, s);
+    else
+      launch_gate_up_t<16, 2>(dm, x, logits, w, ids, wts, h, s);
+  }
   switch (dm.f / 32) {
     case 2: launch_down_slots<2>(dm, ids, wts, h, w, y, s); break;
     case 4: launch_down_slots<4>(dm, ids, wts, h, w, y, s); break;
