@@ -43,6 +43,11 @@ def _setup(cfg):
     G.small_config("graph_prefill_t700", T=700, d=512, f=256, E=64, k=8, seed=42),
     G.small_config("graph_decode_t1", T=1, d=2048, f=512, E=256, k=8, seed=43),
     G.small_config("graph_decode_t5", T=5, d=512, f=256, E=64, k=8, seed=44),
+    # the decode kernels' other splits: one unit per gate/up wavefront with
+    # several slots per down wavefront (T = 3), one down wavefront per
+    # workgroup (T = 12)
+    G.small_config("graph_decode_t3", T=3, d=2048, f=512, E=256, k=8, seed=45),
+    G.small_config("graph_decode_t12", T=12, d=256, f=128, E=32, k=8, seed=46),
 ], ids=lambda c: c.name)
 def test_graph_replays_match_eager(cfg):
     say(f"[graph] {cfg.name}")
