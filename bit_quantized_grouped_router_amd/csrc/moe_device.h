@@ -272,10 +272,79 @@ __device__ __forceinline__ void wave_load_logits(const float *__restrict__ row, 
   }
 }
 
+// Selection for at most 4 logits per lane. Each lane first orders its keys
+// descending with a stable odd-even transposition sort (adjacent swaps only
+// on a strictly larger key, so equal keys keep ascending slots, i.e. the
+// lower expert index first). A round then takes the wavefront maximum of the
+// lanes' first keys; among lanes whose first key equals it, the lowest
+// expert index (no lane holds an equal key further down with a lower index:
+// its first key would equal the maximum too, with a lower slot). The winning
+// lane shifts its list by one. Same result as the general selection below.
+template <int kMaxPerLane>
+__device__ __forceinline__ void wave_topk_sorted(const float (&v)[kMaxPerLane], int E, int k,
+                                                 int *out_id, float *out_logit) {
+  static_assert(kMaxPerLane >= 1 && kMaxPerLane <= 4, "sorted selection: up to 4 keys per lane");
+  constexpr int M = kMaxPerLane;
+  const int lane = threadIdx.x & (kWave - 1);
+  uint32_t key[M];
+  int slot[M];
+#pragma unroll
+  for (int i = 0; i < M; ++i) {
+    key[i] = lane + i * kWave < E ? logit_key(v[i]) : 0u;
+    slot[i] = i;
+  }
+#pragma unroll
+  for (int pass = 0; pass < M; ++pass)
+#pragma unroll
+    for (int i = pass & 1; i + 1 < M; i += 2)
+      if (key[i + 1] > key[i]) {
+        const uint32_t tk = key[i];
+        key[i] = key[i + 1];
+        key[i + 1] = tk;
+        const int ts = slot[i];
+        slot[i] = slot[i + 1];
+        slot[i + 1] = ts;
+      }
+  int my_id = 0;
+  float my_logit = 0.f;
+  for (int j = 0; j < k; ++j) {
+    const uint32_t m = wave_max_u32(key[0]);
+    const uint64_t tied = __builtin_amdgcn_ballot_w64(key[0] == m);
+    int wl;
+    if (__builtin_popcountll(tied) == 1) {
+      wl = __builtin_ctzll(tied);
+    } else {
+      // lowest expert index lane + 64 * slot among the lanes holding key m first
+      const uint32_t idx = (uint32_t)(lane + kWave * slot[0]);
+      wl = (int)(~wave_max_u32(key[0] == m ? ~idx : 0u) & (kWave - 1));
+    }
+    int id = wl + kWave * __builtin_amdgcn_readlane(slot[0], wl);
+    if (id >= E) id = 0;  // unreachable while k <= E; keeps ids in range
+    if (lane == wl) {
+#pragma unroll
+      for (int i = 0; i + 1 < M; ++i) {
+        key[i] = key[i + 1];
+        slot[i] = slot[i + 1];
+      }
+      key[M - 1] = 0u;
+    }
+    if (lane == j) {
+      my_id = id;
+      my_logit = key_logit(m);
+    }
+  }
+  *out_id = my_id;
+  *out_logit = my_logit;
+}
+
 // The selection on logits already in registers (as wave_load_logits leaves them).
 template <int kMaxPerLane>
 __device__ __forceinline__ void wave_topk_loaded(const float (&v)[kMaxPerLane], int E, int k,
                                                  int *out_id, float *out_logit) {
+  if constexpr (kMaxPerLane <= 4) {
+    wave_topk_sorted<kMaxPerLane>(v, E, k, out_id, out_logit);
+    return;
+  }
   const int lane = threadIdx.x & (kWave - 1);
   uint32_t key[kMaxPerLane];
 #pragma unroll
