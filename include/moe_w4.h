@@ -230,7 +230,7 @@ size_t moe_layer_workspace_bytes(const moe_dims *dm);
  * moe_layer_forward - the whole layer on one stream with no host sync:
  * route, permute, gate/up, down, combine, or, for up to 16 tokens, the
  * decode path (two launches, one grid row per token: routing recomputed on
- * chip, each token's 9 experts' 4-bit weights streamed with 128-bit loads;
+ * chip, each token's k + 1 experts' 4-bit weights streamed with 128-bit loads;
  * page section "Prefill e decode: onde estao os ganhos": at small batches
  * bandwidth sets the ceiling). The two paths agree within rounding; the
  * workspace's routing and permutation buffers are only written by the
