@@ -48,6 +48,10 @@ SMALL = [
     # (wavefronts take two or three slots each), and f / 32 = 8 lanes per row
     G.small_config("decode_k20_f256", T=3, d=128, f=256, E=40, k=20, seed=25),
     G.small_config("decode_k32_t16", T=16, d=64, f=64, E=64, k=32, seed=26),
+    # decode kernels over the widest input (three 2048-column passes per row)
+    G.small_config("decode_d6144_t2", T=2, d=6144, f=64, E=4, k=2, seed=27),
+    # the most experts and the largest k the library takes, grouped path
+    G.small_config("max_e1024_k32_t40", T=40, d=64, f=64, E=1024, k=32, seed=28),
 ]
 
 
