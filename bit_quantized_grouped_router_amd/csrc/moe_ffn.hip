@@ -121,8 +121,11 @@ struct TileSetup {
 // landed (at most the NRB DMA chunks of stage kt+1, issued one step later,
 // may still be in flight; code loads issued after them only make the wait
 // stricter), barrier (every wavefront's stage kt is in LDS, and every
-// wavefront is done with stage kt-1), DMA of stage kt+2 into the slot of
-// stage kt-1, code loads for step kt+2, then the four K slices.
+// wavefront's reads of stage kt-1 have completed: the barrier also waits for
+// the wavefront's own LDS operations, since the compiler may leave the last
+// slice's fragment reads in flight past the end of a step), DMA of stage
+// kt+2 into the slot of stage kt-1, code loads for step kt+2, then the four
+// K slices.
 template <int NRB, bool FAST>
 __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
                                             f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
@@ -184,7 +187,9 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   {                                                                                          \
     const int ktv_ = (kt_);                                                                  \
     MOE_WAIT_VMCNT(NRB + 2);                                                                 \
-    __builtin_amdgcn_s_barrier();                                                            \
+    /* the barrier waits for this wavefront's LDS reads too: the DMA issued  */              \
+    /* right after it refills the stage the previous step read from          */              \
+    lds_barrier();                                                                           \
     /* no LDS access or use of this step's codes moves above the wait and barrier */        \
     asm volatile("" : "+v"(cr[slot_][0]), "+v"(cr[slot_][1])::"memory");                    \
     MOE_DMA(ktv_ + 2, (ktv_ + 2) % kStages);                                                 \
@@ -443,9 +448,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
     default: tile_k_loop<kRB>(st, smem, acc, cr0, cr1, fast); break;
   }
 
-  // ---- epilogue. Every wavefront is past its last LDS read of the ring
+  // ---- epilogue. Every wavefront's LDS reads of the ring have completed
   // before any wavefront reuses the LDS.
-  __builtin_amdgcn_s_barrier();
+  lds_barrier();
   asm volatile("" ::: "memory");
   if (!wave_on) return;
   // C layout of the 32x32 MFMA: lane l holds column l%32, register r holds
