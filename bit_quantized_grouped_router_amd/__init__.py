@@ -109,6 +109,42 @@ def _stream(stream) -> int:
     return stream.cuda_stream if hasattr(stream, "cuda_stream") else int(stream)
 
 
+def _need(t: Optional[torch.Tensor], nbytes: int, name: str) -> None:
+    """Raise unless tensor t holds at least nbytes bytes. The kernels index their
+    buffers from the dims alone, so a smaller tensor would be read or written past
+    its end on the device."""
+    if t is None:
+        raise MoeError(f"{name} is missing")
+    have = t.numel() * t.element_size()
+    if have < nbytes:
+        raise MoeError(f"{name} holds {have} bytes; these dims need {nbytes}")
+
+
+def _need_weights(w: "W4Weights", dm: MoeDims) -> None:
+    """Byte sizes of the four int4-g64 tensor sets for dims dm (see include/moe_w4.h)."""
+    d, f, E = dm.d, dm.f, dm.E
+    for name, n, rows, cols in (("w13", E, 2 * f, d), ("w2", E, d, f), ("s13", 1, 2 * f, d),
+                                ("s2", 1, d, f)):
+        m = getattr(w, name)
+        _need(m.codes, n * rows * cols // 2, f"{name}.codes")
+        _need(m.scales, n * rows * (cols // GROUP) * 2, f"{name}.scales")
+        _need(m.biases, n * rows * (cols // GROUP) * 2, f"{name}.biases")
+
+
+def _need_map(dm: MoeDims, tile_map, num_tiles) -> None:
+    _need(tile_map, moe_tile_capacity(dm) * 4 * 4, "tile_map")
+    _need(num_tiles, 4, "num_tiles")
+
+
+def _need_routing(dm: MoeDims, out: Dict) -> None:
+    tk = dm.T * dm.k
+    _need(out.get("counts"), dm.E * 4, "counts")
+    _need(out.get("offsets"), (dm.E + 1) * 4, "offsets")
+    _need(out.get("sorted_token"), tk * 4, "sorted_token")
+    _need(out.get("row_of"), tk * 4, "row_of")
+    _need_map(dm, out.get("tile_map"), out.get("num_tiles"))
+
+
 def dims(T: int, d: int, f: int, E: int, k: int) -> MoeDims:
     return MoeDims(T, d, f, E, k)
 
@@ -172,6 +208,9 @@ def moe_route(logits: torch.Tensor, k: int, topk_ids=None, topk_w=None, stream=N
     dev = logits.device
     topk_ids = torch.empty((T, k), dtype=torch.int32, device=dev) if topk_ids is None else topk_ids
     topk_w = torch.empty((T, k), dtype=torch.float32, device=dev) if topk_w is None else topk_w
+    _need(logits, T * E * 4, "logits")
+    _need(topk_ids, T * k * 4, "topk_ids")
+    _need(topk_w, T * k * 4, "topk_w")
     _check(lib().moe_route(_ptr(logits), T, E, k, _ptr(topk_ids), _ptr(topk_w), _stream(stream)),
            "moe_route")
     return topk_ids, topk_w
@@ -191,6 +230,8 @@ def moe_permute(dm: MoeDims, topk_ids: torch.Tensor, out: Optional[Dict] = None,
     nbytes = moe_permute_workspace_bytes(dm)
     if ws is None:
         ws = torch.empty(max(nbytes, 16), dtype=torch.uint8, device=dev)
+    _need(topk_ids, tk * 4, "topk_ids")
+    _need_routing(dm, out)
     _check(lib().moe_permute(ctypes.byref(dm), _ptr(topk_ids), _ptr(out["counts"]),
                              _ptr(out["offsets"]), _ptr(out["sorted_token"]),
                              _ptr(out["row_of"]), _ptr(out["tile_map"]), _ptr(out["num_tiles"]),
@@ -214,6 +255,10 @@ def moe_route_permute(dm: MoeDims, logits: torch.Tensor, out: Optional[Dict] = N
                "num_tiles": torch.zeros(4, **i32)}
     if ws is None:
         ws = torch.empty(max(moe_permute_workspace_bytes(dm), 16), dtype=torch.uint8, device=dev)
+    _need(logits, dm.T * dm.E * 4, "logits")
+    _need(out.get("ids"), tk * 4, "ids")
+    _need(out.get("wts"), tk * 4, "wts")
+    _need_routing(dm, out)
     _check(lib().moe_route_permute(ctypes.byref(dm), _ptr(logits), _ptr(out["ids"]),
                                    _ptr(out["wts"]), _ptr(out["counts"]), _ptr(out["offsets"]),
                                    _ptr(out["sorted_token"]), _ptr(out["row_of"]),
@@ -226,6 +271,12 @@ def moe_expert_gate_up_w4(dm: MoeDims, x: torch.Tensor, w: W4Weights, sorted_tok
                           num_tiles, h=None, stream=None):
     if h is None:
         h = torch.empty((dm.T * dm.k + dm.T, dm.f), dtype=torch.bfloat16, device=x.device)
+    rows = dm.T * dm.k + dm.T
+    _need(x, dm.T * dm.d * 2, "x")
+    _need(sorted_token, dm.T * dm.k * 4, "sorted_token")
+    _need_map(dm, tile_map, num_tiles)
+    _need(h, rows * dm.f * 2, "h")
+    _need_weights(w, dm)
     _check(lib().moe_expert_gate_up_w4(ctypes.byref(dm), _ptr(x), ctypes.byref(w.c()),
                                        _ptr(sorted_token), _ptr(tile_map), _ptr(num_tiles),
                                        _ptr(h), _stream(stream)), "moe_expert_gate_up_w4")
@@ -239,6 +290,11 @@ def moe_expert_down_w4(dm: MoeDims, h: torch.Tensor, w: W4Weights, tile_map, num
         o_routed = torch.empty((max(dm.T * dm.k, 1), dm.d), dtype=torch.bfloat16, device=dev)
     if o_shared is None:
         o_shared = torch.empty((max(dm.T, 1), dm.d), dtype=torch.float32, device=dev)
+    _need(h, (dm.T * dm.k + dm.T) * dm.f * 2, "h")
+    _need_map(dm, tile_map, num_tiles)
+    _need(o_routed, dm.T * dm.k * dm.d * 2, "o_routed")
+    _need(o_shared, dm.T * dm.d * 4, "o_shared")
+    _need_weights(w, dm)
     _check(lib().moe_expert_down_w4(ctypes.byref(dm), _ptr(h), ctypes.byref(w.c()),
                                     _ptr(tile_map), _ptr(num_tiles), _ptr(o_routed),
                                     _ptr(o_shared), _stream(stream)), "moe_expert_down_w4")
@@ -254,6 +310,13 @@ def moe_expert_ffn_w4(dm: MoeDims, x: torch.Tensor, w: W4Weights, sorted_token, 
         o_routed = torch.empty((max(dm.T * dm.k, 1), dm.d), dtype=torch.bfloat16, device=dev)
     if o_shared is None:
         o_shared = torch.empty((max(dm.T, 1), dm.d), dtype=torch.float32, device=dev)
+    _need(x, dm.T * dm.d * 2, "x")
+    _need(sorted_token, dm.T * dm.k * 4, "sorted_token")
+    _need_map(dm, tile_map, num_tiles)
+    _need(h, (dm.T * dm.k + dm.T) * dm.f * 2, "h")
+    _need(o_routed, dm.T * dm.k * dm.d * 2, "o_routed")
+    _need(o_shared, dm.T * dm.d * 4, "o_shared")
+    _need_weights(w, dm)
     _check(lib().moe_expert_ffn_w4(ctypes.byref(dm), _ptr(x), ctypes.byref(w.c()),
                                    _ptr(sorted_token), _ptr(tile_map), _ptr(num_tiles), _ptr(h),
                                    _ptr(o_routed), _ptr(o_shared), _stream(stream)),
@@ -264,6 +327,11 @@ def moe_expert_ffn_w4(dm: MoeDims, x: torch.Tensor, w: W4Weights, sorted_token, 
 def moe_unpermute_combine(dm: MoeDims, o_routed, o_shared, topk_w, row_of, y=None, stream=None):
     if y is None:
         y = torch.empty((dm.T, dm.d), dtype=torch.float32, device=o_shared.device)
+    _need(o_routed, dm.T * dm.k * dm.d * 2, "o_routed")
+    _need(o_shared, dm.T * dm.d * 4, "o_shared")
+    _need(topk_w, dm.T * dm.k * 4, "topk_w")
+    _need(row_of, dm.T * dm.k * 4, "row_of")
+    _need(y, dm.T * dm.d * 4, "y")
     _check(lib().moe_unpermute_combine(ctypes.byref(dm), _ptr(o_routed), _ptr(o_shared),
                                        _ptr(topk_w), _ptr(row_of), _ptr(y), _stream(stream)),
            "moe_unpermute_combine")
@@ -277,6 +345,11 @@ def moe_layer_forward(dm: MoeDims, x: torch.Tensor, logits: torch.Tensor, w: W4W
         y = torch.empty((dm.T, dm.d), dtype=torch.float32, device=x.device)
     if ws is None:
         ws = torch.empty(max(moe_layer_workspace_bytes(dm), 16), dtype=torch.uint8, device=x.device)
+    _need(x, dm.T * dm.d * 2, "x")
+    _need(logits, dm.T * dm.E * 4, "logits")
+    _need(y, dm.T * dm.d * 4, "y")
+    if wc is None:  # a prebuilt struct (wc) is the caller's to size
+        _need_weights(w, dm)
     wc = w.c() if wc is None else wc
     _check(lib().moe_layer_forward(ctypes.byref(dm), _ptr(x), _ptr(logits), ctypes.byref(wc),
                                    _ptr(y), _ptr(ws), ws.numel(), _stream(stream)),
@@ -290,6 +363,7 @@ def moe_router_logits(x: torch.Tensor, w_router: torch.Tensor, logits=None, stre
     E = w_router.shape[0]
     if logits is None:
         logits = torch.empty((T, E), dtype=torch.float32, device=x.device)
+    _need(logits, T * E * 4, "logits")
     _check(lib().moe_router_logits(_ptr(x), _ptr(w_router), T, d, E, _ptr(logits),
                                    _stream(stream)), "moe_router_logits")
     return logits
@@ -302,6 +376,11 @@ def moe_layer_forward_hidden(dm: MoeDims, x: torch.Tensor, w_router: torch.Tenso
         y = torch.empty((dm.T, dm.d), dtype=torch.float32, device=x.device)
     if ws is None:
         ws = torch.empty(max(moe_layer_workspace_bytes(dm), 16), dtype=torch.uint8, device=x.device)
+    _need(x, dm.T * dm.d * 2, "x")
+    _need(w_router, dm.E * dm.d * 2, "w_router")
+    _need(y, dm.T * dm.d * 4, "y")
+    if wc is None:  # a prebuilt struct (wc) is the caller's to size
+        _need_weights(w, dm)
     wc = w.c() if wc is None else wc
     _check(lib().moe_layer_forward_hidden(ctypes.byref(dm), _ptr(x), _ptr(w_router),
                                           ctypes.byref(wc), _ptr(y), _ptr(ws), ws.numel(),
@@ -314,6 +393,10 @@ def moe_dequant_w4(m: W4Matrix, index: int = 0, out=None, stream=None):
     cols = m.codes.shape[-1] * 2
     if out is None:
         out = torch.empty((rows, cols), dtype=torch.bfloat16, device=m.codes.device)
+    n = m.codes.shape[0] if m.codes.dim() == 3 else 1
+    if not 0 <= index < n:
+        raise MoeError(f"matrix index {index} outside 0..{n - 1}")
+    _need(out, rows * cols * 2, "out")
     cm = m.c(index)
     _check(lib().moe_dequant_w4(ctypes.byref(cm), rows, cols, _ptr(out), _stream(stream)),
            "moe_dequant_w4")

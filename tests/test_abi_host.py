@@ -192,3 +192,53 @@ def test_binding_refuses_cpu_tensors(L):
     import torch
     with pytest.raises(M.MoeError):
         M.moe_route(torch.zeros((4, 8)), 2)
+
+
+def test_binding_checks_buffer_sizes(L):
+    """The binding refuses a tensor smaller than the dims imply (the kernels would
+    index past its end) before it looks at the device; the size check runs on
+    CPU tensors too."""
+    import torch
+
+    T, d, f, E, k = 4, 128, 64, 8, 2
+    dm = M.dims(T, d, f, E, k)
+    # routing (T and E come from the logits' shape): an output one column short
+    with pytest.raises(M.MoeError, match="topk_ids holds"):
+        M.moe_route(torch.zeros((T, E), dtype=torch.float32), k,
+                    topk_ids=torch.zeros((T, k - 1), dtype=torch.int32),
+                    topk_w=torch.zeros((T, k), dtype=torch.float32))
+    # right sizes get past the size check and stop at the device check
+    with pytest.raises(M.MoeError, match="GPU memory"):
+        M.moe_route(torch.zeros((T, E), dtype=torch.float32), k,
+                    topk_ids=torch.zeros((T, k), dtype=torch.int32),
+                    topk_w=torch.zeros((T, k), dtype=torch.float32))
+
+    def weights(short=None):
+        def mat(n, rows, cols, cut):
+            c = torch.zeros(n * rows * cols // 2 - (16 if cut else 0), dtype=torch.uint8)
+            s = torch.zeros(n * rows * cols // 64, dtype=torch.int16)
+            return M.W4Matrix(c, s, s.clone())
+        return M.W4Weights(mat(E, 2 * f, d, short == "w13"), mat(E, d, f, short == "w2"),
+                           mat(1, 2 * f, d, short == "s13"), mat(1, d, f, short == "s2"))
+
+    x = torch.zeros((T, d), dtype=torch.int16)
+    logits = torch.zeros((T, E), dtype=torch.float32)
+    y = torch.zeros((T, d), dtype=torch.float32)
+    ws = torch.zeros(M.moe_layer_workspace_bytes(dm), dtype=torch.uint8)
+    for short in ("w13", "w2", "s13", "s2"):
+        with pytest.raises(M.MoeError, match=f"{short}.codes holds"):
+            M.moe_layer_forward(dm, x, logits, weights(short), y=y, ws=ws)
+    with pytest.raises(M.MoeError, match="y holds"):
+        M.moe_layer_forward(dm, x, logits, weights(), y=torch.zeros((T, d - 1)), ws=ws)
+    with pytest.raises(M.MoeError, match="GPU memory"):
+        M.moe_layer_forward(dm, x, logits, weights(), y=y, ws=ws)
+    # the combine: o_routed one row short
+    with pytest.raises(M.MoeError, match="o_routed holds"):
+        M.moe_unpermute_combine(dm, torch.zeros((T * k - 1, d), dtype=torch.int16),
+                                torch.zeros((T, d)), torch.zeros((T, k)),
+                                torch.zeros(T * k, dtype=torch.int32), y=y)
+    # dequant: matrix index past the stack
+    m = weights().w13
+    with pytest.raises(M.MoeError, match="outside"):
+        M.moe_dequant_w4(M.W4Matrix(m.codes.view(E, 2 * f, d // 2), m.scales.view(E, 2 * f, d // 64),
+                                    m.biases.view(E, 2 * f, d // 64)), index=E)
