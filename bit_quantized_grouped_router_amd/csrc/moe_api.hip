@@ -37,8 +37,11 @@ moe_status check_ptr(const void *p) {
 
 moe_status check_dims(const moe_dims *dm) {
   if (dm == nullptr) return MOE_E_INVALID;
-  if (dm->T < 0 || dm->d <= 0 || dm->f <= 0 || dm->E <= 0 || dm->k <= 0) return MOE_E_INVALID;
+  if (dm->T < 0 || dm->d <= 0 || dm->f <= 0 || dm->E <= 0 || dm->k <= 0 || dm->f_shared <= 0)
+    return MOE_E_INVALID;
   if (dm->k > dm->E) return MOE_E_INVALID;
+  // a shared expert of another width is a valid layer these kernels do not run
+  if (dm->f_shared != dm->f) return MOE_E_UNSUPPORTED;
   if (dm->d % kGroup != 0 || dm->f % kGroup != 0) return MOE_E_UNSUPPORTED;
   if (dm->E > 1024 || dm->k > 32) return MOE_E_UNSUPPORTED;
   if (dm->d > kGemmMaxK || dm->f > kGemmMaxK) return MOE_E_UNSUPPORTED;

@@ -111,6 +111,20 @@ struct TileSetup {
   int nrb;                // active 32-row blocks of the tile (1..kRB), wave-uniform
 };
 
+// Schedule check build (MOE_SCHED_CHECK=1, a separate library made by the
+// build for a regression test): a scheduling barrier after each K step's
+// loads pushes more of the step's A-fragment LDS reads towards its end, up to
+// the next step's barrier. The results must stay bit-identical, which holds
+// only while every barrier of the loop also waits for the wavefront's own LDS
+// reads (the stage they read is refilled by the DMA issued right after it).
+#if defined(MOE_SCHED_CHECK) && MOE_SCHED_CHECK
+#define MOE_SCHED_CHECK_POINT() __builtin_amdgcn_sched_barrier(0)
+#else
+#define MOE_SCHED_CHECK_POINT() \
+  do {                          \
+  } while (0)
+#endif
+
 // K loop of one tile. NRB: the tile's active 32-row blocks (1..kRB), known
 // at compile time, so a short tile moves, reads and multiplies only the rows
 // it has (the activation DMA, the A-fragment reads and the MFMAs all scale
@@ -194,6 +208,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
     asm volatile("" : "+v"(cr[slot_][0]), "+v"(cr[slot_][1])::"memory");                    \
     MOE_DMA(ktv_ + 2, (ktv_ + 2) % kStages);                                                 \
     MOE_LOAD_B(ktv_ + 2, ((slot_) + 2) % 3);                                                 \
+    MOE_SCHED_CHECK_POINT();                                                                 \
     const uint32_t s0_ = sb0, s1_ = sb1;                                                     \
     {                                                                                        \
       const int kn_ = min(ktv_ + 1, klast) * kWgCols + st.lr0;                               \

@@ -31,11 +31,13 @@
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *
  * Shapes (moe_dims)
- *   T tokens, d hidden size, f expert width (the shared expert has width f
- *   too), E routed experts, k experts chosen per token.
+ *   T tokens, d hidden size, f routed expert width, f_shared the shared
+ *   expert's width, E routed experts, k experts chosen per token.
  *   Limits: T >= 0, d % 64 == 0, f % 64 == 0, d <= 6144, f <= 6144,
  *   1 <= k <= min(E, 32), 1 <= E <= 1024, T*(k+1) < 2^31 and every tensor
- *   under 2^31 elements.
+ *   under 2^31 elements. f_shared must equal f (a different shared width is
+ *   a valid layer this version does not run: MOE_E_UNSUPPORTED; f_shared <= 0
+ *   is MOE_E_INVALID).
  *
  * Weight layout (moe_w4_matrix), canonical and unshuffled
  *   codes  uint8 [n][rows][cols/2]: column c of a row is byte c>>1, in the
@@ -71,11 +73,12 @@ typedef enum {
 } moe_status;
 
 typedef struct {
-  int32_t T; /* tokens */
-  int32_t d; /* hidden size (input of gate/up, output of down) */
-  int32_t f; /* expert intermediate width, routed and shared */
-  int32_t E; /* routed experts */
-  int32_t k; /* experts chosen per token */
+  int32_t T;        /* tokens */
+  int32_t d;        /* hidden size (input of gate/up, output of down) */
+  int32_t f;        /* routed expert intermediate width */
+  int32_t E;        /* routed experts */
+  int32_t k;        /* experts chosen per token */
+  int32_t f_shared; /* shared expert intermediate width; must equal f */
 } moe_dims;
 
 typedef struct {
@@ -87,8 +90,8 @@ typedef struct {
 typedef struct {
   moe_w4_matrix w13; /* routed gate|up: n = E, rows = 2f (gate rows 0..f-1, up rows f..2f-1), cols = d */
   moe_w4_matrix w2;  /* routed down:    n = E, rows = d, cols = f */
-  moe_w4_matrix s13; /* shared gate|up: n = 1, rows = 2f, cols = d */
-  moe_w4_matrix s2;  /* shared down:    n = 1, rows = d, cols = f */
+  moe_w4_matrix s13; /* shared gate|up: n = 1, rows = 2 f_shared, cols = d */
+  moe_w4_matrix s2;  /* shared down:    n = 1, rows = d, cols = f_shared */
 } moe_w4_weights;
 
 /*

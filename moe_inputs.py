@@ -54,6 +54,13 @@ TAG_S2_SCALES = 23
 TAG_DEC_X = 30
 TAG_DEC_LOGITS = 31
 TAG_ROUTER = 40
+# bias patterns of the general-bias weight modes: tag of the scale stream + this
+TAG_BIAS_OFFSET = 1000
+
+# weight bias modes (make_w4)
+BIAS_NEG8 = "neg8"        # bias = -8 * scale exactly (the workloads' format)
+BIAS_GENERAL = "general"  # every group draws its own bias (see make_w4)
+BIAS_MIXED = "mixed"      # rows of -8 * scale groups, with some rows of general groups
 
 
 @dataclasses.dataclass(frozen=True)
@@ -70,6 +77,7 @@ class MoeConfig:
     seed: int = 0
     scale_lo: float = 0.005
     scale_hi: float = 0.02
+    bias_mode: str = BIAS_NEG8   # how the weights' biases are drawn (make_w4)
 
     @property
     def f_shared(self) -> int:
@@ -109,26 +117,68 @@ def bf16_bits_times(bits: np.ndarray, factor: float) -> np.ndarray:
 
 
 def make_w4(seed: int, tag_codes: int, tag_scales: int, n: int, rows: int, cols: int,
-            scale_lo: float, scale_hi: float) -> Dict[str, np.ndarray]:
-    """Random int4-g64 matrices: uniform codes 0..15, scale ~ U(lo, hi) in bf16, bias = -8*scale.
+            scale_lo: float, scale_hi: float, bias_mode: str = BIAS_NEG8) -> Dict[str, np.ndarray]:
+    """Random int4-g64 matrices: uniform codes 0..15 and one (scale, bias) per 64 columns.
 
     Uniform random bytes give two independent uniform 4-bit codes per byte.
+    bias_mode:
+      neg8     scale ~ U(lo, hi) in bf16 and bias = -8 * scale (exact in bf16);
+      general  every group draws its own pair, all in bf16:
+                 scale: |s| ~ U(lo, hi), negative for 10% of the groups; 2% of
+                   the groups take a tiny scale (|s| * 2^-104) and 2% a scale
+                   2^-24 times smaller than their bias (|b| ~ hi * U(1/16, 16));
+                 bias: -s * U(1/16, 16) for most groups; +0 for 5% and -0 for
+                   2% of them; -8 * s for 3%; -s * U(0, 2^-6) for 2%;
+               no value is an fp32 subnormal;
+               so both exact dequantisation paths of the kernels (and the
+               switches between them) occur, while the weights keep magnitudes
+               near the neg8 ones;
+      mixed    neg8 rows with 1% of the weight rows (all their groups) drawn as
+               in general, so a block of 64 rows is neg8-only about half the time.
     """
     assert cols % GROUP == 0
     codes = rng(seed, tag_codes).integers(0, 256, size=(n, rows, cols // 2), dtype=np.uint8)
-    s32 = rng(seed, tag_scales).uniform(scale_lo, scale_hi, size=(n, rows, cols // GROUP))
-    scales = f32_to_bf16_bits(s32.astype(np.float32))
-    biases = bf16_bits_times(scales, -8.0)
-    return {"codes": codes, "scales": scales, "biases": biases}
+    shape = (n, rows, cols // GROUP)
+    s32 = rng(seed, tag_scales).uniform(scale_lo, scale_hi, size=shape)
+    if bias_mode == BIAS_NEG8:
+        scales = f32_to_bf16_bits(s32.astype(np.float32))
+        biases = bf16_bits_times(scales, -8.0)
+        return {"codes": codes, "scales": scales, "biases": biases}
+    assert bias_mode in (BIAS_GENERAL, BIAS_MIXED), bias_mode
+    r = rng(seed, tag_scales + TAG_BIAS_OFFSET)
+    u_sign, u_scale, u_bias = r.random(shape), r.random(shape), r.random(shape)
+    frac = r.uniform(1.0 / 16.0, 16.0, size=shape)
+    small = r.uniform(0.0, 2.0 ** -6, size=shape)
+    s = np.where(u_sign < 0.1, -s32, s32)
+    tiny = u_scale < 0.02                      # scale exponent far below the usual range
+    far = (u_scale >= 0.02) & (u_scale < 0.04)  # bias 2^24 times the scale
+    s = np.where(tiny, s * 2.0 ** -104, s)
+    b = -s * frac
+    b = np.where(far, -np.sign(s) * frac * scale_hi, b)
+    s = np.where(far, s * 2.0 ** -24, s)
+    b = np.where((u_bias >= 0.10) & (u_bias < 0.12) & ~tiny & ~far, -s * small, b)
+    b = np.where(u_bias < 0.05, 0.0, b)
+    b = np.where((u_bias >= 0.05) & (u_bias < 0.07), -0.0, b)
+    scales = f32_to_bf16_bits(s.astype(np.float32))
+    biases = f32_to_bf16_bits(b.astype(np.float32))
+    neg8 = (u_bias >= 0.07) & (u_bias < 0.10) & ~far
+    biases = np.where(neg8, bf16_bits_times(scales, -8.0), biases)
+    if bias_mode == BIAS_MIXED:
+        general_row = r.random((n, rows, 1)) < 0.01
+        s_neg8 = f32_to_bf16_bits(s32.astype(np.float32))
+        b_neg8 = bf16_bits_times(s_neg8, -8.0)
+        scales = np.where(general_row, scales, s_neg8)
+        biases = np.where(general_row, biases, b_neg8)
+    return {"codes": codes, "scales": scales.astype(np.uint16), "biases": biases.astype(np.uint16)}
 
 
 def make_weights(cfg: MoeConfig) -> Dict[str, Dict[str, np.ndarray]]:
-    s, lo, hi = cfg.seed, cfg.scale_lo, cfg.scale_hi
+    s, lo, hi, bm = cfg.seed, cfg.scale_lo, cfg.scale_hi, cfg.bias_mode
     return {
-        "w13": make_w4(s, TAG_W13_CODES, TAG_W13_SCALES, cfg.E, 2 * cfg.f, cfg.d, lo, hi),
-        "w2": make_w4(s, TAG_W2_CODES, TAG_W2_SCALES, cfg.E, cfg.d, cfg.f, lo, hi),
-        "s13": make_w4(s, TAG_S13_CODES, TAG_S13_SCALES, 1, 2 * cfg.f_shared, cfg.d, lo, hi),
-        "s2": make_w4(s, TAG_S2_CODES, TAG_S2_SCALES, 1, cfg.d, cfg.f_shared, lo, hi),
+        "w13": make_w4(s, TAG_W13_CODES, TAG_W13_SCALES, cfg.E, 2 * cfg.f, cfg.d, lo, hi, bm),
+        "w2": make_w4(s, TAG_W2_CODES, TAG_W2_SCALES, cfg.E, cfg.d, cfg.f, lo, hi, bm),
+        "s13": make_w4(s, TAG_S13_CODES, TAG_S13_SCALES, 1, 2 * cfg.f_shared, cfg.d, lo, hi, bm),
+        "s2": make_w4(s, TAG_S2_CODES, TAG_S2_SCALES, 1, cfg.d, cfg.f_shared, lo, hi, bm),
     }
 
 
@@ -186,7 +236,8 @@ def make_decode_steps(cfg: MoeConfig, steps: Optional[int] = None) -> Dict[str, 
 
 
 def small_config(name: str, T: int, d: int, f: int, E: int, k: int, seed: int,
-                 zipf_s: float = 0.0, n_forced_empty: int = 0) -> MoeConfig:
+                 zipf_s: float = 0.0, n_forced_empty: int = 0,
+                 bias_mode: str = BIAS_NEG8) -> MoeConfig:
     """An ad-hoc configuration for tests (random small shapes)."""
     return MoeConfig(name, T=T, d=d, f=f, E=E, k=k, zipf_s=zipf_s,
-                     n_forced_empty=n_forced_empty, seed=seed)
+                     n_forced_empty=n_forced_empty, seed=seed, bias_mode=bias_mode)

@@ -1,5 +1,6 @@
 """Helpers of the GPU parity tests: device upload, read-back and the tolerance checks."""
 import sys
+from concurrent.futures import ThreadPoolExecutor
 
 import numpy as np
 import torch
@@ -74,3 +75,20 @@ def expected_schedule(tiles) -> np.ndarray:
     tiles = np.asarray(tiles)
     heights = tiles[:, 2] - tiles[:, 1]
     return np.array(sorted(range(len(tiles)), key=lambda i: (-int(heights[i]), i)), dtype=np.int64)
+
+
+def fill_expert_cache(weights, experts, cache, threads: int = 8):
+    """Dequantise the given routed experts (and the shared one) with the oracle, in
+    threads (numpy releases the interpreter lock inside the large array operations),
+    into ``cache`` under the keys O.token_outputs uses: g for routed expert g, -1 for
+    the shared expert."""
+    todo = [int(g) for g in experts if int(g) not in cache]
+
+    def one(g):
+        return g, (O.dequant_expert(weights["w13"], g), O.dequant_expert(weights["w2"], g))
+
+    with ThreadPoolExecutor(threads) as ex:
+        for g, mats in ex.map(one, todo):
+            cache[g] = mats
+    if -1 not in cache:
+        cache[-1] = (O.dequant_expert(weights["s13"], 0), O.dequant_expert(weights["s2"], 0))

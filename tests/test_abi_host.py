@@ -51,8 +51,8 @@ def test_library_has_gfx950_code_only():
     assert not re.search(r"gfx9[0-4]\d\b", out.stdout.replace("gfx950", ""))
 
 
-def _dims(T=16, d=128, f=64, E=8, k=2):
-    return M.MoeDims(T, d, f, E, k)
+def _dims(T=16, d=128, f=64, E=8, k=2, f_shared=None):
+    return M.MoeDims(T, d, f, E, k, f if f_shared is None else f_shared)
 
 
 def test_block_m_and_capacity(L):
@@ -91,6 +91,7 @@ def test_dims_validation(L):
     assert f(ctypes.byref(_dims(f=96))) == 0
     assert f(ctypes.byref(_dims(E=2000))) == 0
     assert f(ctypes.byref(_dims(k=9))) == 0
+    assert f(ctypes.byref(_dims(f_shared=0))) == 0
     assert f(ctypes.byref(_dims())) > 0
     assert L.moe_tile_capacity(ctypes.byref(_dims(d=100))) == -1
     # workspace grows with T
@@ -115,6 +116,14 @@ def test_layer_forward_validation(L):
     assert fw(ctypes.byref(_dims(d=6208)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
     assert fw(ctypes.byref(_dims(f=6208)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == UNSUPPORTED
     assert fw(ctypes.byref(dm), FAKE, FAKE, None, FAKE, FAKE, need, None) == INVALID
+    # the shared expert's width: another width is a valid layer these kernels do not run
+    assert fw(ctypes.byref(_dims(f_shared=128)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need,
+              None) == UNSUPPORTED
+    assert fw(ctypes.byref(_dims(f_shared=0)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need,
+              None) == INVALID
+    assert fw(ctypes.byref(_dims(f_shared=-64)), FAKE, FAKE, ctypes.byref(w), FAKE, FAKE, need,
+              None) == INVALID
+    assert L.moe_tile_capacity(ctypes.byref(_dims(f_shared=128))) == -1
     assert fw(ctypes.byref(dm), None, FAKE, ctypes.byref(w), FAKE, FAKE, need, None) == INVALID
     assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(_weights(FAKE + 2)), FAKE, FAKE, need, None) == ALIGN
     assert fw(ctypes.byref(dm), FAKE, FAKE, ctypes.byref(w), FAKE + 8, FAKE, need, None) == ALIGN
@@ -242,3 +251,42 @@ def test_binding_checks_buffer_sizes(L):
     with pytest.raises(M.MoeError, match="outside"):
         M.moe_dequant_w4(M.W4Matrix(m.codes.view(E, 2 * f, d // 2), m.scales.view(E, 2 * f, d // 64),
                                     m.biases.view(E, 2 * f, d // 64)), index=E)
+
+
+def test_binding_checks_element_types(L):
+    """Each tensor is read as one fixed element type; a tensor of another type (an
+    fp32 x would have its bits read as bf16) is refused before any device access."""
+    import torch
+
+    T, d, f, E, k = 4, 128, 64, 8, 2
+    dm = M.dims(T, d, f, E, k)
+    with pytest.raises(M.MoeError, match="logits has dtype"):
+        M.moe_route(torch.zeros((T, E), dtype=torch.float64), k)
+    with pytest.raises(M.MoeError, match="topk_ids has dtype"):
+        M.moe_route(torch.zeros((T, E)), k, topk_ids=torch.zeros((T, k), dtype=torch.int64),
+                    topk_w=torch.zeros((T, k)))
+    with pytest.raises(M.MoeError, match="x has dtype"):
+        M.moe_router_logits(torch.zeros((T, d), dtype=torch.float32),
+                            torch.zeros((E, d), dtype=torch.bfloat16))
+    with pytest.raises(M.MoeError, match="x has dtype"):
+        M.moe_router_logits(torch.zeros((T, d), dtype=torch.float16),
+                            torch.zeros((E, d), dtype=torch.bfloat16))
+    # the router matrix must have x's width and E full rows
+    with pytest.raises(M.MoeError, match="columns"):
+        M.moe_router_logits(torch.zeros((T, d), dtype=torch.bfloat16),
+                            torch.zeros((E, d - 64), dtype=torch.bfloat16))
+    with pytest.raises(M.MoeError, match="GPU memory"):
+        M.moe_router_logits(torch.zeros((T, d), dtype=torch.bfloat16),
+                            torch.zeros((E, d), dtype=torch.bfloat16))
+    # dequant: scales and biases sized and typed
+    codes = torch.zeros((1, 2 * f, d // 2), dtype=torch.uint8)
+    sc = torch.zeros((1, 2 * f, d // 64), dtype=torch.int16)
+    with pytest.raises(M.MoeError, match="scales holds"):
+        M.moe_dequant_w4(M.W4Matrix(codes, sc[:, :f], sc))
+    with pytest.raises(M.MoeError, match="biases has dtype"):
+        M.moe_dequant_w4(M.W4Matrix(codes, sc, sc.float()))
+    # the layer: an fp32 x
+    ws = torch.zeros(M.moe_layer_workspace_bytes(dm), dtype=torch.uint8)
+    with pytest.raises(M.MoeError, match="x has dtype"):
+        M.moe_layer_forward(dm, torch.zeros((T, d)), torch.zeros((T, E)), None,
+                            y=torch.zeros((T, d)), ws=ws)

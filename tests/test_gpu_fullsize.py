@@ -14,7 +14,8 @@ import torch
 import bit_quantized_grouped_router_amd as M
 import moe_inputs as G
 from oracle import moe_oracle as O
-from parity_util import W_ABS, check_y, dev_bits, expected_schedule, say, upload
+from parity_util import (W_ABS, check_y, dev_bits, expected_schedule, fill_expert_cache, say,
+                         upload)
 
 pytestmark = pytest.mark.gpu
 
@@ -69,13 +70,28 @@ def test_full_size_prefill(name):
     yh = y.cpu().numpy()
     assert np.isfinite(yh).all()
     r = np.random.default_rng(5)
-    # sampled tokens: some random, plus tokens routed to the most loaded expert
+    # sampled tokens: for every non-empty expert, the token of its last permuted
+    # row (so the last, possibly partial, tile of every group is checked: every
+    # tile between 33 and 127 rows is such a tile), of its first row and of one
+    # random row; tokens routed to the most loaded expert; the first and last
+    # tokens, and 20 random ones
     rid, _ = O.route(inp["logits"], cfg.k)
+    offsets = O.exclusive_scan(counts)
+    st, _ = O.scatter(rid, offsets)
+    picks = [r.choice(cfg.T, 20, replace=False), [0, cfg.T - 1]]
+    for g in np.nonzero(counts)[0]:
+        lo, hi = int(offsets[g]), int(offsets[g + 1])
+        picks.append([st[lo], st[hi - 1], st[r.integers(lo, hi)]])
     top = int(np.argmax(counts))
     heavy = np.nonzero((rid == top).any(axis=1))[0]
-    toks = np.unique(np.concatenate([r.choice(cfg.T, 20, replace=False), heavy[:4], heavy[-4:],
-                                     [0, cfg.T - 1]]))
-    say(f"[full size] {name}: oracle on {len(toks)} tokens")
+    picks += [heavy[:4], heavy[-4:]]
+    toks = np.unique(np.concatenate([np.asarray(p, dtype=np.int64) for p in picks]))
+    # every non-empty expert is checked on at least one of its rows
+    checked = np.unique(rid[toks])
+    assert set(np.nonzero(counts)[0]) <= set(checked.tolist())
+    say(f"[full size] {name}: oracle on {len(toks)} tokens covering all "
+        f"{int((counts > 0).sum())} non-empty experts")
+    fill_expert_cache(inp["weights"], checked, _cache)
     ref = O.token_outputs(inp["x"], inp["logits"], inp["weights"], cfg.k, toks, cache=_cache)
     check_y(yh[toks], ref, f"y[{len(toks)} sampled tokens]")
 
@@ -90,17 +106,18 @@ def test_decode_b1():
     rid, rw = O.route(steps["logits"], cfg.k)
     assert np.array_equal(ids.cpu().numpy(), rid)
     assert np.abs(wts.cpu().numpy() - rw).max() <= W_ABS
-    say("[decode] y on 48 seeded steps through the T=1 path")
+    say("[decode] y on 64 seeded steps through the T=1 path")
     w = M.W4Weights.from_numpy(weights)
     dm = M.dims(1, cfg.d, cfg.f, cfg.E, cfg.k)
     ws = torch.empty(M.moe_layer_workspace_bytes(dm), dtype=torch.uint8, device="cuda")
     x_all = dev_bits(steps["x"])
-    pick = np.sort(np.random.default_rng(7).choice(cfg.decode_steps, 48, replace=False))
+    pick = np.sort(np.random.default_rng(7).choice(cfg.decode_steps, 64, replace=False))
     ys = []
     for s in pick:
         ys.append(M.moe_layer_forward(dm, x_all[s:s + 1], logits_all[s:s + 1], w, ws=ws).clone())
     torch.cuda.synchronize()
     y = torch.cat(ys).cpu().numpy()
+    fill_expert_cache(weights, np.unique(rid[pick]), _cache)
     ref = O.token_outputs(steps["x"], steps["logits"], weights, cfg.k, pick, cache=_cache)
     check_y(y, ref, "decode y")
     # the T=1 path agrees with the prefill kernels run on the same single token

@@ -12,6 +12,7 @@ import pytest
 import torch
 
 import bit_quantized_grouped_router_amd as M
+import bias_cases
 import moe_inputs as G
 from oracle import moe_oracle as O
 from parity_util import (W_ABS, check_bf16_close, check_y, dev_bits, expected_schedule, host_bits, say,
@@ -181,7 +182,13 @@ def _h_slack(cfg, inp, ref):
     return slack
 
 
-@pytest.mark.parametrize("cfg", SMALL, ids=lambda c: c.name)
+# general and mixed dequantisation biases (the plain K loops of both grouped
+# GEMMs at every row-block count, and the per-group plain branch of the decode
+# and small-batch kernels)
+GENERAL_BIAS = bias_cases.ALL
+
+
+@pytest.mark.parametrize("cfg", SMALL + GENERAL_BIAS, ids=lambda c: c.name)
 def test_expert_ffn_and_combine(cfg):
     say(f"[ffn] {cfg.name}")
     ref = oracle(cfg)
@@ -221,7 +228,8 @@ def test_expert_ffn_and_combine(cfg):
     assert np.abs(y - y_ref).max() <= 1e-5 * np.sqrt(np.mean(y_ref ** 2))
 
 
-@pytest.mark.parametrize("cfg", SMALL + [G.CONFIGS["prefill_t512"]], ids=lambda c: c.name)
+@pytest.mark.parametrize("cfg", SMALL + GENERAL_BIAS + [G.CONFIGS["prefill_t512"]],
+                         ids=lambda c: c.name)
 def test_layer_forward_matches_oracle(cfg):
     say(f"[layer] {cfg.name}")
     inp = inputs(cfg)
