@@ -24,7 +24,7 @@ EXPORTS = [
     "moe_permute", "moe_expert_gate_up_w4", "moe_expert_down_w4", "moe_expert_ffn_w4",
     "moe_unpermute_combine", "moe_layer_workspace_bytes", "moe_layer_forward",
     "moe_dequant_w4", "moe_status_string", "moe_last_hip_error", "moe_router_logits",
-    "moe_layer_forward_hidden", "moe_route_permute",
+    "moe_layer_forward_hidden", "moe_route_permute", "moe_layer_forward_noalloc",
 ]
 
 
@@ -70,6 +70,7 @@ def load(path: str) -> ctypes.CDLL:
         "moe_unpermute_combine": ([D, P, P, P, P, P, P], I32),
         "moe_layer_workspace_bytes": ([D], SZ),
         "moe_layer_forward": ([D, P, P, W, P, P, SZ, P], I32),
+        "moe_layer_forward_noalloc": ([D, P, P, W, P, P], I32),
         "moe_router_logits": ([P, P, I32, I32, I32, P, P], I32),
         "moe_layer_forward_hidden": ([D, P, P, W, P, P, SZ, P], I32),
         "moe_route_permute": ([D, P, P, P, P, P, P, P, P, P, P, SZ, P], I32),
@@ -385,6 +386,22 @@ def moe_layer_forward(dm: MoeDims, x: torch.Tensor, logits: torch.Tensor, w: W4W
     _check(lib().moe_layer_forward(ctypes.byref(dm), _ptr(x), _ptr(logits), ctypes.byref(wc),
                                    _ptr(y), _ptr(ws), ws.numel() * ws.element_size(), _stream(stream)),
            "moe_layer_forward")
+    return y
+
+
+def moe_layer_forward_noalloc(dm: MoeDims, x: torch.Tensor, logits: torch.Tensor, w: W4Weights,
+                              y: torch.Tensor, stream=None, wc: Optional[MoeW4Weights] = None):
+    """One layer call with the library's own device scratch (no workspace, nothing
+    allocated by the call: y must be given)."""
+    _need(x, dm.T * dm.d * 2, "x", BF16)
+    _need(logits, dm.T * dm.E * 4, "logits", F32)
+    _need(y, dm.T * dm.d * 4, "y", F32)
+    if wc is None:  # a prebuilt struct (wc) is the caller's to size
+        _need_weights(w, dm)
+    wc = w.c() if wc is None else wc
+    _check(lib().moe_layer_forward_noalloc(ctypes.byref(dm), _ptr(x), _ptr(logits),
+                                           ctypes.byref(wc), _ptr(y), _stream(stream)),
+           "moe_layer_forward_noalloc")
     return y
 
 

@@ -4,6 +4,7 @@
 #include <hip/hip_runtime.h>
 
 #include <cstdint>
+#include <mutex>
 
 #include "../../include/moe_w4.h"
 #include "moe_launch.h"
@@ -129,6 +130,35 @@ LayerWs carve_layer(const Dims &dm, char *base) {
   w.logits = take<float>(base, off, (size_t)dm.T * dm.E);  // router scores (hidden-state entry)
   w.bytes = off;
   return w;
+}
+
+// Scratch of moe_layer_forward_noalloc: one copy per GPU, loaded with the
+// library's code object and held until the process ends. Host code never uses
+// the array's name as an address (on the host it is a stand-in, not device
+// memory): each device's address comes from hipGetSymbolAddress, taken once
+// per device with that device current, and is kept below.
+static __device__ __align__(256) uint8_t scratch[MOE_NOALLOC_SCRATCH_BYTES];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// This device's address of the scratch array (looked up on the first call).
+moe_status scratch_address(void **out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_status(e);
+  if (dev < 0 || dev >= kMaxDevices) return MOE_E_UNSUPPORTED;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void *p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_status(e);
+    if (p == nullptr || ((uintptr_t)p & 255u) != 0) return MOE_E_ALIGN;
+    g_scratch_ptr[dev] = p;
+  }
+  *out = g_scratch_ptr[dev];
+  return MOE_OK;
 }
 
 }  // namespace
@@ -301,6 +331,23 @@ moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float 
   const Dims d = to_dims(dm);
   const LayerWs L = carve_layer(d, (char *)ws);
   if (ws_bytes < L.bytes) return MOE_E_WORKSPACE;
+  return enqueue_layer(d, x, logits, to_weights(w), y, L, as_stream(stream));
+}
+
+moe_status moe_layer_forward_noalloc(const moe_dims *dm, const uint16_t *x, const float *logits,
+                                     const moe_w4_weights *w, float *y, void *stream) {
+  MOE_TRY(check_dims(dm));
+  if (dm->T == 0) return MOE_OK;
+  MOE_TRY(check_weights(w, true, true));
+  MOE_TRY(check_ptr(x));
+  MOE_TRY(check_ptr(logits));
+  MOE_TRY(check_ptr(y));
+  const Dims d = to_dims(dm);
+  // the size check comes before any HIP call
+  if (carve_layer(d, nullptr).bytes > (size_t)MOE_NOALLOC_SCRATCH_BYTES) return MOE_E_WORKSPACE;
+  void *base = nullptr;
+  MOE_TRY(scratch_address(&base));
+  const LayerWs L = carve_layer(d, (char *)base);
   return enqueue_layer(d, x, logits, to_weights(w), y, L, as_stream(stream));
 }
 

@@ -26,8 +26,10 @@
  *   - Every pointer must be 16-byte aligned (MOE_E_ALIGN otherwise).
  *   - Outputs must not alias inputs.
  *   - No C++ exception crosses this interface. Apart from a thread-local last
- *     error the library holds no mutable state, so calls on different
- *     streams or threads are safe when their buffers do not overlap.
+ *     error and the device scratch of moe_layer_forward_noalloc (with its
+ *     per-device address table), the library holds no mutable state, so calls
+ *     on different streams or threads are safe when their buffers do not
+ *     overlap.
  *   - bf16 tensors are passed as uint16_t bit patterns.
  *
  * Shapes (moe_dims)
@@ -246,6 +248,34 @@ size_t moe_layer_workspace_bytes(const moe_dims *dm);
 moe_status moe_layer_forward(const moe_dims *dm, const uint16_t *x, const float *logits,
                              const moe_w4_weights *w, float *y, void *ws, size_t ws_bytes,
                              void *stream);
+
+/* Bytes of the library's own device scratch array used by
+ * moe_layer_forward_noalloc (one array per GPU the library runs on). */
+#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/*
+ * moe_layer_forward_noalloc - moe_layer_forward for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation): the same kernels and results, with the
+ * scratch taken from a device array the library owns instead of a caller
+ * workspace. The call allocates nothing.
+ *   x, logits, w, y  as moe_layer_forward (the caller still owns all of them)
+ * Limits: the layer's scratch (moe_layer_workspace_bytes of the dims) must fit
+ * in MOE_NOALLOC_SCRATCH_BYTES = 64 MiB, otherwise MOE_E_WORKSPACE is returned
+ * before any HIP call. At d = 2048, f = 512, E = 256, k = 8 that is T <= 1307
+ * (every T that takes the decode path fits).
+ * The array: one per GPU, loaded with the library's code object and kept until
+ * the process ends; its device address is looked up (hipGetSymbolAddress) on
+ * the first call on each device, with that device current, so the stream must
+ * belong to the current device. Every call on a GPU shares that GPU's array and
+ * leaves its contents behind; nothing in it has to start at zero (every piece
+ * is written before it is read within a call). Calls that may overlap on one
+ * GPU (two streams, two threads, two captured graphs replayed concurrently)
+ * race on the array: order them, or use moe_layer_forward with separate
+ * workspaces.
+ */
+moe_status moe_layer_forward_noalloc(const moe_dims *dm, const uint16_t *x, const float *logits,
+                                     const moe_w4_weights *w, float *y, void *stream);
 
 /*
  * moe_layer_forward_hidden - moe_layer_forward starting from hidden states:

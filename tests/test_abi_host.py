@@ -290,3 +290,22 @@ def test_binding_checks_element_types(L):
     with pytest.raises(M.MoeError, match="x has dtype"):
         M.moe_layer_forward(dm, torch.zeros((T, d)), torch.zeros((T, E)), None,
                             y=torch.zeros((T, d)), ws=ws)
+
+
+def test_noalloc_validation(L):
+    """The no-allocation layer call validates like moe_layer_forward and refuses, before
+    any HIP call, a layer whose scratch exceeds the library's static array."""
+    w = _weights()
+    fn = L.moe_layer_forward_noalloc
+    assert fn(ctypes.byref(_dims(T=0)), None, None, ctypes.byref(w), None, None) == OK
+    assert fn(ctypes.byref(_dims(d=100)), FAKE, FAKE, ctypes.byref(w), FAKE, None) == UNSUPPORTED
+    assert fn(ctypes.byref(_dims()), None, FAKE, ctypes.byref(w), FAKE, None) == INVALID
+    assert fn(ctypes.byref(_dims()), FAKE, FAKE, ctypes.byref(w), FAKE + 4, None) == ALIGN
+    limit = 64 << 20
+    big = _dims(T=1308, d=2048, f=512, E=256, k=8)
+    assert L.moe_layer_workspace_bytes(ctypes.byref(big)) > limit
+    assert fn(ctypes.byref(big), FAKE, FAKE, ctypes.byref(w), FAKE, None) == WORKSPACE
+    fits = _dims(T=1307, d=2048, f=512, E=256, k=8)
+    assert L.moe_layer_workspace_bytes(ctypes.byref(fits)) <= limit
+    header = open(HEADER).read()
+    assert "#define MOE_NOALLOC_SCRATCH_BYTES (64u << 20)" in header

@@ -1,0 +1,70 @@
+"""moe_layer_forward_noalloc (the layer with the library's own device scratch,
+for callers that cannot allocate) through the C ABI, against
+moe_layer_forward with a caller workspace: the same kernels, so the same bits.
+
+Calls follow each other on one GPU, each smaller than the one before, so each
+call runs over what the previous one left in the shared scratch array.
+"""
+import numpy as np
+import pytest
+import torch
+
+import bit_quantized_grouped_router_amd as M
+import moe_inputs as G
+from oracle import moe_oracle as O
+from parity_util import check_y, say, upload
+
+pytestmark = pytest.mark.gpu
+
+CALLS = [
+    # the headline widths near the scratch limit (T <= 1307 at these dims)
+    G.small_config("na_full_width_t1200", T=1200, d=2048, f=512, E=256, k=8, seed=91,
+                   zipf_s=1.1),
+    # smaller: grouped path with mixed dequantisation biases
+    G.small_config("na_t300_mixed", T=300, d=256, f=128, E=16, k=4, seed=92, zipf_s=1.1,
+                   bias_mode=G.BIAS_MIXED),
+    # smaller still: the batch-1 decode path
+    G.small_config("na_t1", T=1, d=2048, f=512, E=256, k=8, seed=93),
+]
+
+
+@pytest.fixture(scope="module", autouse=True)
+def _gpu():
+    if not torch.cuda.is_available():
+        pytest.skip("no GPU")
+    M.lib()
+    yield
+    torch.cuda.synchronize()
+
+
+def test_noalloc_matches_layer_forward_on_successive_calls():
+    for cfg in CALLS:
+        say(f"[noalloc] {cfg.name}")
+        inp = G.make_layer_inputs(cfg)
+        dm, x, logits, w = upload(inp)
+        y_ws = M.moe_layer_forward(dm, x, logits, w)
+        y = torch.full((cfg.T, cfg.d), float("nan"), dtype=torch.float32, device="cuda")
+        M.moe_layer_forward_noalloc(dm, x, logits, w, y)
+        torch.cuda.synchronize()
+        assert torch.equal(y, y_ws), f"{cfg.name}: differs from moe_layer_forward"
+        if cfg.T * cfg.d <= 300 * 256 or cfg.T == 1:
+            ref = O.layer_forward(inp["x"], inp["logits"], inp["weights"], cfg.k,
+                                  BM=M.moe_block_m())["y"]
+            check_y(y.cpu().numpy(), ref, f"{cfg.name} y")
+        # a second call on the same inputs gives the same bits
+        y2 = torch.full_like(y, float("nan"))
+        M.moe_layer_forward_noalloc(dm, x, logits, w, y2)
+        torch.cuda.synchronize()
+        assert torch.equal(y2, y)
+
+
+def test_noalloc_refuses_layers_past_its_scratch():
+    cfg = G.small_config("na_too_big", T=1308, d=2048, f=512, E=256, k=8, seed=94)
+    dm = M.dims(cfg.T, cfg.d, cfg.f, cfg.E, cfg.k)
+    x = torch.zeros((cfg.T, cfg.d), dtype=torch.int16, device="cuda")
+    logits = torch.zeros((cfg.T, cfg.E), dtype=torch.float32, device="cuda")
+    y = torch.zeros((cfg.T, cfg.d), dtype=torch.float32, device="cuda")
+    w = M.W4Weights.from_numpy(G.make_weights(G.small_config("na_w", T=1, d=2048, f=512, E=256,
+                                                              k=8, seed=94)))
+    with pytest.raises(M.MoeError, match="workspace too small"):
+        M.moe_layer_forward_noalloc(dm, x, logits, w, y)
