@@ -6,12 +6,18 @@ Headline: MoE-layer prefill tokens/s at T=4096 (d=2048, f=512, E=256, top-8
 step, inputs resident in HBM. Also reported on the same JSON line:
   roofline      the gate/up grouped GEMM (the dominant kernel): algorithmic
                 FLOP per launch / its mean duration (HIP events on the stream
-                the kernel runs on), against the 2.5 PFLOP/s bf16 dense peak;
+                the kernel runs on), against the 2516.6 TFLOP/s bf16 dense peak;
   kernels       every kernel's mean duration and rate;
   decode        batch-1 decode: 1000 steps through the T=1 path, 32 weight
                 copies rotated so no step re-reads weights from cache, replayed
                 as a HIP graph; algorithmic bytes / time per step;
-  cpu_baseline  the CPU oracle on a bounded sample of the same workload;
+  configs       the other workloads: T=16 (median latency), T=512 (two
+                weight copies alternated; GB/s of the used experts' weights and
+                I/O against 8 TB/s), T=16384 with 8 forced-empty experts
+                (TFLOP/s against the bf16 peak, per-kernel times);
+  mixed_bias    the headline layer with mixed dequantisation biases;
+  cpu_baseline  the CPU oracle on the whole headline layer (and, under
+                configs, on the whole layer of each other workload);
   small_batch   (--small-batch) the layer at T = 1 .. 64, bytes of the used
                 experts' weights / time.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
@@ -26,7 +32,7 @@ import time
 ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
-PEAK_BF16_TFLOPS = 2500.0     # MI355X dense bf16 MFMA
+PEAK_BF16_TFLOPS = 2516.6     # MI355X dense bf16 MFMA: 256 CUs x 2.4 GHz x 4096 FLOP/clock
 PEAK_HBM_GBPS = 8000.0        # MI355X HBM3E
 W4_BYTES_PER_EXPERT = None    # filled from the shapes
 
@@ -67,6 +73,67 @@ def traffic_from_profile(sources, launches_key):
     return None
 
 
+def event_us(fn, n, stream, warm=3):
+    """Per-call durations (us) of fn() with HIP events on `stream`, all calls enqueued
+    before one synchronisation."""
+    import torch
+    for _ in range(warm):
+        fn()
+    evs = []
+    for _ in range(n):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record(stream)
+        fn()
+        b.record(stream)
+        evs.append((a, b))
+    torch.cuda.synchronize()
+    return [a.elapsed_time(b) * 1e3 for a, b in evs]
+
+
+def median(v):
+    v = sorted(v)
+    return v[len(v) // 2] if len(v) % 2 else 0.5 * (v[len(v) // 2 - 1] + v[len(v) // 2])
+
+
+def kernel_times(M, dm, x, logits, w, n_iter, stream):
+    """Mean duration (us) of each kernel of the layer, HIP events around each call on
+    `stream` (all iterations enqueued before one synchronisation)."""
+    import torch
+    k = dm.k
+    ids, wts = M.moe_route(logits, k, stream=stream)
+    perm = M.moe_permute(dm, ids, stream=stream)
+    h, o_r, o_sh = M.moe_expert_ffn_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
+                                       perm["num_tiles"], stream=stream)
+    yk = M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], stream=stream)
+    torch.cuda.synchronize()
+    names = ["route", "permute", "gate_up", "down", "combine"]
+    acc = {n: 0.0 for n in names}
+    evs = []
+    for it in range(n_iter + 2):
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+        ev[0].record(stream)
+        M.moe_route(logits, k, ids, wts, stream=stream)
+        ev[1].record(stream)
+        M.moe_permute(dm, ids, out=perm, stream=stream)
+        ev[2].record(stream)
+        M.moe_expert_gate_up_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
+                                perm["num_tiles"], h=h, stream=stream)
+        ev[3].record(stream)
+        M.moe_expert_down_w4(dm, h, w, perm["tile_map"], perm["num_tiles"], o_routed=o_r,
+                             o_shared=o_sh, stream=stream)
+        ev[4].record(stream)
+        M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk, stream=stream)
+        ev[5].record(stream)
+        if it >= 2:
+            evs.append(ev)
+    torch.cuda.synchronize()
+    for ev in evs:
+        for i, n in enumerate(names):
+            acc[n] += ev[i].elapsed_time(ev[i + 1]) * 1e3 / len(evs)
+    nonempty = int((perm["counts"] > 0).sum().item())
+    return acc, nonempty
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -74,11 +141,13 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--decode-steps", type=int, default=1000)
     ap.add_argument("--no-decode", action="store_true")
+    ap.add_argument("--no-configs", action="store_true",
+                    help="skip the other workloads (T=16, T=512, T=16384) and the mixed-bias row")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-headline-only", action="store_true",
+                    help="time the CPU oracle on the headline layer only")
     ap.add_argument("--small-batch", action="store_true",
-                    help="also time moe_layer_forward at T = 1, 2, 8, 32, 64 (off by default so the "
-                         "grouped GEMMs' profiled means stay those of the T=4096 launch)")
-    ap.add_argument("--cpu-sample-tokens", type=int, default=2048)
+                    help="also time moe_layer_forward at T = 1, 2, 8, 32, 64")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -101,6 +170,7 @@ def main():
     assert torch.cuda.is_available(), "bench.py needs a GPU"
     torch.cuda.set_device(0)
     dev = torch.device("cuda", 0)
+    stream = torch.cuda.current_stream()
 
     if args.calibrate_copy:
         src = torch.ones(64 << 20, dtype=torch.float32, device=dev)
@@ -110,21 +180,27 @@ def main():
         log(f"[bench] calibration copy: {src.numel() * 4} bytes read and written")
         del src, dst
 
+    def upload(cfg, weights=None):
+        a = G.make_activations(cfg)
+        x = torch.from_numpy(a["x"].view(np.int16)).to(dev)
+        lg = torch.from_numpy(a["logits"]).to(dev)
+        wt = weights if weights is not None else G.make_weights(cfg)
+        return a, x, lg, wt, M.W4Weights.from_numpy(wt, device=dev)
+
+    def flops(T, d, f, k):
+        rows = T * (k + 1)
+        return 2.0 * rows * d * 2 * f, 2.0 * rows * f * d
+
     cfg = G.CONFIGS["prefill_t4096_zipf"]
     T, d, f, E, k = cfg.T, cfg.d, cfg.f, cfg.E, cfg.k
     log(f"[bench] generating {cfg.name}")
-    inp = G.make_layer_inputs(cfg)
-    x = torch.from_numpy(inp["x"].view(np.int16)).to(dev)
-    logits = torch.from_numpy(inp["logits"]).to(dev)
-    w = M.W4Weights.from_numpy(inp["weights"], device=dev)
+    act, x, logits, weights_np, w = upload(cfg)
+    inp = {"x": act["x"], "logits": act["logits"], "weights": weights_np}
     wc = w.c()
     dm = M.dims(T, d, f, E, k)
     ws = torch.empty(M.moe_layer_workspace_bytes(dm), dtype=torch.uint8, device=dev)
     y = torch.empty((T, d), dtype=torch.float32, device=dev)
-
-    rows = T * (k + 1)
-    flop_gate_up = 2.0 * rows * d * 2 * f
-    flop_down = 2.0 * rows * f * d
+    flop_gate_up, flop_down = flops(T, d, f, k)
     flop_layer = flop_gate_up + flop_down
 
     # ---------------------------------------------------------------- headline: whole layer
@@ -143,76 +219,126 @@ def main():
 
     # ---------------------------------------------------------------- per-kernel timing
     log("[bench] per-kernel timing with HIP events")
-    ids, wts = M.moe_route(logits, k)
-    perm = M.moe_permute(dm, ids)
-    h, o_r, o_sh = M.moe_expert_ffn_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
-                                       perm["num_tiles"])
-    yk = M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"])
-    torch.cuda.synchronize()
-    nonempty = int((perm["counts"] > 0).sum().item())
+    acc, nonempty = kernel_times(M, dm, x, logits, w, max(args.steps, 5), stream)
     bytes_layer = ((nonempty + 1) * expert_bytes(d, f) + x.numel() * 2 + logits.numel() * 4
                    + y.numel() * 4)
-    stream = torch.cuda.current_stream()
-    names = ["route", "permute", "gate_up", "down", "combine"]
-    acc = {n: 0.0 for n in names}
-    n_iter = max(args.steps, 5)
-    # all iterations are enqueued before one synchronisation, so the GPU runs
-    # them back to back and each event pair brackets only its kernels
-    evs = []
-    for it in range(n_iter + 2):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
-        ev[0].record(stream)
-        M.moe_route(logits, k, ids, wts, stream=stream)
-        ev[1].record(stream)
-        M.moe_permute(dm, ids, out=perm, stream=stream)
-        ev[2].record(stream)
-        M.moe_expert_gate_up_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
-                                perm["num_tiles"], h=h, stream=stream)
-        ev[3].record(stream)
-        M.moe_expert_down_w4(dm, h, w, perm["tile_map"], perm["num_tiles"], o_routed=o_r,
-                             o_shared=o_sh, stream=stream)
-        ev[4].record(stream)
-        M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"], y=yk, stream=stream)
-        ev[5].record(stream)
-        if it >= 2:
-            evs.append(ev)
-    torch.cuda.synchronize()
-    for ev in evs:
-        for i, n in enumerate(names):
-            acc[n] += ev[i].elapsed_time(ev[i + 1]) / len(evs)
-    kernels = {}
-    for n in names:
-        us = acc[n] * 1e3
-        kernels[n] = {"us": round(us, 2)}
-    kernels["gate_up"]["TFLOP/s"] = round(flop_gate_up / (acc["gate_up"] / 1e3) / 1e12, 1)
-    kernels["down"]["TFLOP/s"] = round(flop_down / (acc["down"] / 1e3) / 1e12, 1)
+    kernels = {n: {"us": round(v, 2)} for n, v in acc.items()}
+    kernels["gate_up"]["TFLOP/s"] = round(flop_gate_up / (acc["gate_up"] * 1e-6) / 1e12, 1)
+    kernels["gate_up"]["frac_bf16_peak"] = round(kernels["gate_up"]["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
+    kernels["down"]["TFLOP/s"] = round(flop_down / (acc["down"] * 1e-6) / 1e12, 1)
+    kernels["down"]["frac_bf16_peak"] = round(kernels["down"]["TFLOP/s"] / PEAK_BF16_TFLOPS, 4)
     comb_bytes = T * k * d * 2 + T * d * 4 * 2 + T * k * 8
-    kernels["combine"]["GB/s"] = round(comb_bytes / (acc["combine"] / 1e3) / 1e9, 1)
+    kernels["combine"]["GB/s"] = round(comb_bytes / (acc["combine"] * 1e-6) / 1e9, 1)
     # router projection (the step before routing when the layer starts from
     # hidden states); timed on its own, the headline step starts from logits
     wr = torch.from_numpy(G.make_router(cfg).view(np.int16)).to(dev)
     lg = torch.empty((T, E), dtype=torch.float32, device=dev)
-    M.moe_router_logits(x, wr, logits=lg, stream=stream)
-    rev = []
-    for it in range(n_iter + 2):
-        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
-        ev[0].record(stream)
-        M.moe_router_logits(x, wr, logits=lg, stream=stream)
-        ev[1].record(stream)
-        if it >= 2:
-            rev.append(ev)
-    torch.cuda.synchronize()
-    us = sum(a.elapsed_time(b) for a, b in rev) / len(rev) * 1e3
+    us = sum(event_us(lambda: M.moe_router_logits(x, wr, logits=lg, stream=stream),
+                      max(args.steps, 5), stream)) / max(args.steps, 5)
+    rflop = 2.0 * T * d * E
     kernels["router_logits"] = {"us": round(us, 2),
-                                "TFLOP/s": round(2.0 * T * d * E / (us / 1e6) / 1e12, 1),
-                                "GB/s": round((T * d * 2 + E * d * 2 + T * E * 4) / (us / 1e6) / 1e9, 1)}
+                                "TFLOP/s": round(rflop / (us * 1e-6) / 1e12, 1),
+                                "frac_bf16_peak": round(rflop / (us * 1e-6) / 1e12
+                                                        / PEAK_BF16_TFLOPS, 4),
+                                "GB/s": round((T * d * 2 + E * d * 2 + T * E * 4) / (us * 1e-6)
+                                              / 1e9, 1)}
     log(f"[bench] kernels: {kernels}")
-    achieved = flop_gate_up / (acc["gate_up"] / 1e3) / 1e12
+    achieved = flop_gate_up / (acc["gate_up"] * 1e-6) / 1e12
     roofline = {"kernel": "gate_up_kernel", "bound": "mfma", "achieved": round(achieved, 2),
                 "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
                 "frac": round(achieved / PEAK_BF16_TFLOPS, 4),
                 "traffic": traffic_from_profile(GEMM_SOURCES, "gate_up_prefill_t4096_zipf"),
                 "algorithmic_flop_per_launch": flop_gate_up}
+
+    # ---------------------------------------------------------------- the other workloads
+    configs = None
+    mixed = None
+    big = None
+    if not args.no_configs:
+        configs = {}
+        # tiny layer: per-call latency
+        c0 = G.CONFIGS["tiny_t16"]
+        a0, x0, l0, w0np, w0 = upload(c0)
+        dm0 = M.dims(c0.T, c0.d, c0.f, c0.E, c0.k)
+        ws0 = torch.empty(M.moe_layer_workspace_bytes(dm0), dtype=torch.uint8, device=dev)
+        y0 = torch.empty((c0.T, c0.d), dtype=torch.float32, device=dev)
+        t = event_us(lambda: M.moe_layer_forward(dm0, x0, l0, w0, y=y0, ws=ws0, stream=stream),
+                     100, stream)
+        configs["tiny_t16"] = {"T": c0.T, "us_median": round(median(t), 2),
+                               "tok/s": round(c0.T / (median(t) * 1e-6), 1),
+                               "_inputs": (a0, w0np)}
+        log(f"[bench] tiny_t16: {configs['tiny_t16']['us_median']} us")
+        # T = 512, near-uniform routing: every expert used; two weight copies
+        # alternated so consecutive calls do not find the weights in the caches
+        c1 = G.CONFIGS["prefill_t512"]
+        a1, x1, l1, w1np, w1 = upload(c1)
+        w1b = M.W4Weights(*[M.W4Matrix(m.codes.clone(), m.scales.clone(), m.biases.clone())
+                            for m in (w1.w13, w1.w2, w1.s13, w1.s2)])
+        wcs1 = [w1.c(), w1b.c()]
+        dm1 = M.dims(c1.T, c1.d, c1.f, c1.E, c1.k)
+        ws1 = torch.empty(M.moe_layer_workspace_bytes(dm1), dtype=torch.uint8, device=dev)
+        y1 = torch.empty((c1.T, c1.d), dtype=torch.float32, device=dev)
+        it = [0]
+
+        def call1():
+            M.moe_layer_forward(dm1, x1, l1, None, y=y1, ws=ws1, wc=wcs1[it[0] % 2],
+                                stream=stream)
+            it[0] += 1
+
+        t = event_us(call1, 50, stream)
+        ne1 = len(np.unique(M.moe_route(l1, c1.k)[0].cpu().numpy()))
+        by1 = ((ne1 + 1) * expert_bytes(c1.d, c1.f) + c1.T * (c1.d * 2 + c1.E * 4 + c1.d * 4))
+        fl1 = sum(flops(c1.T, c1.d, c1.f, c1.k))
+        us1 = median(t)
+        configs["prefill_t512"] = {
+            "T": c1.T, "bound": "hbm", "us_median": round(us1, 2),
+            "tok/s": round(c1.T / (us1 * 1e-6), 1), "nonempty_experts": ne1,
+            "algorithmic_bytes": by1, "GB/s": round(by1 / (us1 * 1e-6) / 1e9, 1),
+            "frac_hbm": round(by1 / (us1 * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
+            "TFLOP/s": round(fl1 / (us1 * 1e-6) / 1e12, 1), "weight_copies": 2,
+            "_inputs": (a1, w1np)}
+        log(f"[bench] prefill_t512: "
+            f"{ {k_: v for k_, v in configs['prefill_t512'].items() if k_ != '_inputs'} }")
+        del w1b, wcs1
+        # T = 16384, skewed routing with 8 forced-empty experts
+        c4 = G.CONFIGS["prefill_t16384_zipf_empty"]
+        a4, x4, l4, w4np, w4 = upload(c4, weights=weights_np)  # same weights (same seed and shapes)
+        dm4 = M.dims(c4.T, c4.d, c4.f, c4.E, c4.k)
+        ws4 = torch.empty(M.moe_layer_workspace_bytes(dm4), dtype=torch.uint8, device=dev)
+        y4 = torch.empty((c4.T, c4.d), dtype=torch.float32, device=dev)
+        t = event_us(lambda: M.moe_layer_forward(dm4, x4, l4, w4, y=y4, ws=ws4, stream=stream),
+                     20, stream)
+        us4 = median(t)
+        fg4, fd4 = flops(c4.T, c4.d, c4.f, c4.k)
+        acc4, ne4 = kernel_times(M, dm4, x4, l4, w4, 5, stream)
+        configs["prefill_t16384_zipf_empty"] = {
+            "T": c4.T, "bound": "mfma", "us_median": round(us4, 2),
+            "tok/s": round(c4.T / (us4 * 1e-6), 1), "nonempty_experts": ne4,
+            "TFLOP/s": round((fg4 + fd4) / (us4 * 1e-6) / 1e12, 1),
+            "frac_bf16_peak": round((fg4 + fd4) / (us4 * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "kernels": {n: round(v, 2) for n, v in acc4.items()},
+            "gate_up_frac_bf16_peak": round(fg4 / (acc4["gate_up"] * 1e-6) / 1e12
+                                            / PEAK_BF16_TFLOPS, 4),
+            "down_frac_bf16_peak": round(fd4 / (acc4["down"] * 1e-6) / 1e12 / PEAK_BF16_TFLOPS, 4),
+            "_inputs": (a4, w4np)}
+        log(f"[bench] prefill_t16384_zipf_empty: "
+            f"{ {k_: v for k_, v in configs['prefill_t16384_zipf_empty'].items() if k_ != '_inputs'} }")
+        del x4, l4, w4, ws4, y4
+        # the headline layer with mixed dequantisation biases (some weight rows
+        # with general biases: those wavefronts take the plain dequantisation)
+        cm = G.MoeConfig("prefill_t4096_zipf_mixed_bias", T=T, d=d, f=f, E=E, k=k, zipf_s=1.1,
+                         bias_mode=G.BIAS_MIXED)
+        wm = M.W4Weights.from_numpy(G.make_weights(cm), device=dev)
+        t = event_us(lambda: M.moe_layer_forward(dm, x, logits, wm, y=y, ws=ws, stream=stream),
+                     20, stream)
+        accm, _ = kernel_times(M, dm, x, logits, wm, 5, stream)
+        mixed = {"workload": "prefill_t4096_zipf with mixed biases: 1% of the weight rows draw a "
+                             "general bf16 bias per group, the rest bias = -8 scale",
+                 "us_median": round(median(t), 2),
+                 "TFLOP/s": round(flop_layer / (median(t) * 1e-6) / 1e12, 1),
+                 "kernels": {n: round(v, 2) for n, v in accm.items()}}
+        log(f"[bench] mixed biases: {mixed}")
+        del wm
 
     # ---------------------------------------------------------------- small batches
     # moe_layer_forward at T = 1 .. 64 (the general path; T = 1 takes the
@@ -220,7 +346,7 @@ def main():
     small = None
     if args.small_batch:
         log("[bench] small batches")
-        w2 = M.W4Weights.from_numpy(inp["weights"], device=dev)
+        w2 = M.W4Weights.from_numpy(weights_np, device=dev)
         wcs = [wc, w2.c()]
         small = {}
         for Ts in (1, 2, 8, 32, 64):
@@ -264,14 +390,14 @@ def main():
                                                    m.biases.clone())
                                         for m in (wd.w13, wd.w2, wd.s13, wd.s2)]))
         cstructs = [c.c() for c in copies]
-        dm1 = M.dims(1, dcfg.d, dcfg.f, dcfg.E, dcfg.k)
-        ws1 = torch.empty(M.moe_layer_workspace_bytes(dm1), dtype=torch.uint8, device=dev)
+        dmd = M.dims(1, dcfg.d, dcfg.f, dcfg.E, dcfg.k)
+        wsd = torch.empty(M.moe_layer_workspace_bytes(dmd), dtype=torch.uint8, device=dev)
         yd = torch.empty((args.decode_steps, dcfg.d), dtype=torch.float32, device=dev)
 
-        def run_steps(lo, hi):
+        def run_steps(lo, hi, st=None):
             for s in range(lo, hi):
-                M.moe_layer_forward(dm1, xs[s:s + 1], ls[s:s + 1], None, y=yd[s:s + 1], ws=ws1,
-                                    wc=cstructs[s % n_copies])
+                M.moe_layer_forward(dmd, xs[s:s + 1], ls[s:s + 1], None, y=yd[s:s + 1], ws=wsd,
+                                    wc=cstructs[s % n_copies], stream=st)
 
         run_steps(0, min(64, args.decode_steps))
         torch.cuda.synchronize()
@@ -292,7 +418,7 @@ def main():
                 for lo in range(0, args.decode_steps, chunk):
                     g = torch.cuda.CUDAGraph()
                     with torch.cuda.graph(g, stream=gs):
-                        run_steps(lo, min(lo + chunk, args.decode_steps))
+                        run_steps(lo, min(lo + chunk, args.decode_steps), st=gs)
                     graphs.append(g)
             torch.cuda.synchronize()
             for g in graphs[:2]:
@@ -327,17 +453,32 @@ def main():
             cores = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
         except Exception:
             cores = os.cpu_count()
-        n = min(args.cpu_sample_tokens, T)
-        log(f"[bench] CPU oracle on the first {n} tokens")
-        c0 = time.perf_counter()
-        O.layer_forward(inp["x"][:n], inp["logits"][:n], inp["weights"], k, BM=M.moe_block_m())
-        c1 = time.perf_counter()
-        cpu = {"value": round(n / (c1 - c0), 2), "unit": "tok/s", "cores": cores,
-               "kind": "oracle",
-               "sample": f"first {n} of the {T} tokens of {cfg.name}: the whole oracle layer "
-                         f"(route, permute, dequantise every used expert, fp64 FFNs, combine), "
-                         f"{c1 - c0:.1f} s; host cores granted "
-                         f"{len(os.sched_getaffinity(0))}"}
+        granted = len(os.sched_getaffinity(0))
+
+        def oracle_time(a, wt, c):
+            t_ = time.perf_counter()
+            O.layer_forward(a["x"], a["logits"], wt, c.k, BM=M.moe_block_m())
+            return time.perf_counter() - t_
+
+        log(f"[bench] CPU oracle on the whole {cfg.name} layer")
+        dt = oracle_time(inp, weights_np, cfg)
+        cpu = {"value": round(T / dt, 2), "unit": "tok/s", "cores": cores, "kind": "oracle",
+               "sample": f"the whole {cfg.name} layer ({T} tokens; route, permute, dequantise "
+                         f"every used expert, fp64 FFNs, combine) in {dt:.1f} s; host cores "
+                         f"granted {granted}, BLAS threads {cores}"}
+        if configs is not None and not args.cpu_headline_only:
+            for name, c_ in (("tiny_t16", G.CONFIGS["tiny_t16"]),
+                             ("prefill_t512", G.CONFIGS["prefill_t512"]),
+                             ("prefill_t16384_zipf_empty",
+                              G.CONFIGS["prefill_t16384_zipf_empty"])):
+                a_, wt_ = configs[name]["_inputs"]
+                log(f"[bench] CPU oracle on the whole {name} layer")
+                dt_ = oracle_time(a_, wt_, c_)
+                configs[name]["cpu_oracle"] = {"s": round(dt_, 3),
+                                               "tok/s": round(c_.T / dt_, 2), "cores": cores}
+    if configs is not None:
+        for v in configs.values():
+            v.pop("_inputs", None)
 
     out = {
         "metric": "MoE-layer prefill tok/s @T=4096 (% bf16 MFMA peak); decode B=1 HBM GB/s",
@@ -364,6 +505,8 @@ def main():
                   "GB/s": round(bytes_layer / (ms_per_step / 1e3) / 1e9, 1)},
         "roofline": roofline,
         "kernels": kernels,
+        "configs": configs,
+        "mixed_bias": mixed,
         "decode": decode,
         "small_batch": small,
         "cpu_baseline": cpu,
