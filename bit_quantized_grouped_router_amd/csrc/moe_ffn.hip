@@ -287,6 +287,84 @@ __device__ __forceinline__ void tile_k_loop(const TileSetup &st, uint8_t *lds,
     gemm_k_loop<NRB, false>(st, lds, acc, cr0, cr1);
 }
 
+// Stores one wavefront's block of results: acc[rb][0..1] for the tile's first
+// nrb row blocks. colbase: gate/up, the first of 32 units (acc[.][0] holds
+// their gate rows and acc[.][1] their up rows); down, the first of 64 output
+// columns (acc[.][0] columns colbase .. +31, acc[.][1] the next 32). bf16
+// outputs go through the LDS region ep as [row][col] tiles and leave as
+// 16-byte row chunks; the shared expert's fp32 down outputs are stored
+// directly.
+template <int KIND>
+__device__ __forceinline__ void store_block(const f32x16_t (&acc)[kRB][2], int nrb, int colbase,
+                                            bool shared, int row_begin, int row_end, int TK,
+                                            int d, int f, uint8_t *ep, uint16_t *out_bf16,
+                                            float *out_f32) {
+  const int lane = threadIdx.x & 63;
+  // C layout of the 32x32 MFMA: lane l holds column l%32, register r holds
+  // row 8*(r/4) + 4*(l/32) + r%4
+  const int c = lane & 31, hh = lane >> 5;
+  if (KIND == kDown && shared) {
+    // fp32 rows of the shared expert: 128 contiguous bytes per half-wavefront
+    const int wrow0 = colbase + c, wrow1 = colbase + 32 + c;
+#pragma unroll
+    for (int rb = 0; rb < kRB; ++rb) {
+      if (rb >= nrb) continue;
+#pragma unroll
+      for (int r = 0; r < 16; ++r) {
+        const int p = row_begin + rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
+        if (p >= row_end) continue;
+        out_f32[(size_t)(p - TK) * d + wrow0] = acc[rb][0][r];
+        out_f32[(size_t)(p - TK) * d + wrow1] = acc[rb][1][r];
+      }
+    }
+    return;
+  }
+  // gate/up: 32 columns (64 bytes) per row, physical row r ^ (2 * ((r / 4) %
+  // 2)); down: 64 columns (128 bytes) per row, 16-byte chunk j stored at j ^
+  // (4 * ((r / 4) % 2)). Either way the two halves of the wavefront (rows r
+  // and r + 4) write disjoint banks.
+#pragma unroll
+  for (int rb = 0; rb < kRB; ++rb) {
+    if (rb >= nrb) continue;
+#pragma unroll
+    for (int r = 0; r < 16; r += 2) {
+      const int row = rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);  // even; row + 1 is r + 1's
+      if (KIND == kGateUp) {
+        const uint32_t pk = pack_bf16x2(silu_mul_fast(acc[rb][0][r], acc[rb][1][r]),
+                                        silu_mul_fast(acc[rb][0][r + 1], acc[rb][1][r + 1]));
+        const int pr = row ^ (((row >> 2) & 1) << 1);
+        *(uint16_t *)(ep + pr * 64 + c * 2) = (uint16_t)pk;
+        *(uint16_t *)(ep + (pr + 1) * 64 + c * 2) = (uint16_t)(pk >> 16);
+      } else {
+        const int sw = ((row >> 2) & 1) * 4;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          const uint32_t pk = pack_bf16x2(acc[rb][b][r], acc[rb][b][r + 1]);
+          const int off = ((((b * 32 + c) >> 3) ^ sw) << 4) + (c & 7) * 2;
+          *(uint16_t *)(ep + row * 128 + off) = (uint16_t)pk;
+          *(uint16_t *)(ep + (row + 1) * 128 + off) = (uint16_t)(pk >> 16);
+        }
+      }
+    }
+  }
+  if (KIND == kGateUp) {
+    for (int it = 0; it < nrb * 2; ++it) {
+      const int r = it * 16 + (lane >> 2), j = lane & 3;
+      const int pr = r ^ (((r >> 2) & 1) << 1);
+      const uint4 v = *(const uint4 *)(ep + pr * 64 + j * 16);
+      const int p = row_begin + r;
+      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * f + colbase + j * 8) = v;
+    }
+  } else {
+    for (int it = 0; it < nrb * 4; ++it) {
+      const int r = it * 8 + (lane >> 3), j = lane & 7;
+      const uint4 v = *(const uint4 *)(ep + r * 128 + ((j ^ (((r >> 2) & 1) * 4)) << 4));
+      const int p = row_begin + r;
+      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * d + colbase + j * 8) = v;
+    }
+  }
+}
+
 template <int KIND>
 __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
     const uint16_t *__restrict__ act, W4 wr, W4 ws, const int32_t *__restrict__ sorted_token,
@@ -327,6 +405,10 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
   }
   st.ksteps = K / kKT;
   const int klast = st.ksteps - 1;
+  // the tile's active 32-row blocks (the same for every wavefront: the DMA
+  // fills each row block with all four), clamped to 1..kRB for any map
+  const int rows = row_end - row_begin;
+  const int tile_rb = min(max((rows + 31) / 32, 1), kRB);
   // ---- prologue. The loads go out in dependency order so that their
   // latencies overlap: token indices (they gate the activation DMA), codes of
   // steps 0 and 1 and the tile's scales (they need only the tile), then the
@@ -406,10 +488,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
       st.a_off[i] = ((uint32_t)t * (uint32_t)K + j * 8u) * 2u;  // token clamped: in range for any routing
     }
   }
-  // the tile's active 32-row blocks (the same for every wavefront: the DMA
-  // fills each row block with all four), clamped to 1..kRB for any map
-  const int rows = row_end - row_begin;
-  const int tile_rb = min(max((rows + 31) / 32, 1), kRB);
+  // the DMA of stages 0 and 1
   switch (tile_rb) {
     case 1: prologue_dma<1>(st, smem, klast); break;
     case 2: prologue_dma<2>(st, smem, klast); break;
@@ -468,72 +547,9 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
   lds_barrier();
   asm volatile("" ::: "memory");
   if (!wave_on) return;
-  // C layout of the 32x32 MFMA: lane l holds column l%32, register r holds
-  // row 8*(r/4) + 4*(l/32) + r%4
-  const int c = lane & 31, hh = lane >> 5;
-  if (KIND == kDown && shared) {
-    // fp32 rows of the shared expert: 128 contiguous bytes per half-wavefront
-#pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
-      if (rb >= st.nrb) continue;
-#pragma unroll
-      for (int r = 0; r < 16; ++r) {
-        const int p = row_begin + rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);
-        if (p >= row_end) continue;
-        out_f32[(size_t)(p - TK) * d + wrow0] = acc[rb][0][r];
-        out_f32[(size_t)(p - TK) * d + wrow1] = acc[rb][1][r];
-      }
-    }
-    return;
-  }
-  // bf16 outputs go through this wavefront's LDS region as [row][col] tiles
-  // and leave as 16-byte row chunks. gate/up: 32 columns (64 bytes) per row,
-  // physical row r ^ (2 * ((r / 4) % 2)); down: 64 columns (128 bytes) per
-  // row, 16-byte chunk j stored at j ^ (4 * ((r / 4) % 2)). Either way the
-  // two halves of the wavefront (rows r and r + 4) write disjoint banks.
   uint8_t *ep = smem + wave * (KIND == kGateUp ? kBlockM * 64 : kBlockM * 128);
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
-    if (rb >= st.nrb) continue;
-#pragma unroll
-    for (int r = 0; r < 16; r += 2) {
-      const int row = rb * 32 + (r >> 2) * 8 + hh * 4 + (r & 3);  // even; row + 1 is r + 1's
-      if (KIND == kGateUp) {
-        const uint32_t pk = pack_bf16x2(silu_mul_fast(acc[rb][0][r], acc[rb][1][r]),
-                                        silu_mul_fast(acc[rb][0][r + 1], acc[rb][1][r + 1]));
-        const int pr = row ^ (((row >> 2) & 1) << 1);
-        *(uint16_t *)(ep + pr * 64 + c * 2) = (uint16_t)pk;
-        *(uint16_t *)(ep + (pr + 1) * 64 + c * 2) = (uint16_t)(pk >> 16);
-      } else {
-        const int sw = ((row >> 2) & 1) * 4;
-#pragma unroll
-        for (int b = 0; b < 2; ++b) {
-          const uint32_t pk = pack_bf16x2(acc[rb][b][r], acc[rb][b][r + 1]);
-          const int off = ((((b * 32 + c) >> 3) ^ sw) << 4) + (c & 7) * 2;
-          *(uint16_t *)(ep + row * 128 + off) = (uint16_t)pk;
-          *(uint16_t *)(ep + (row + 1) * 128 + off) = (uint16_t)(pk >> 16);
-        }
-      }
-    }
-  }
-  if (KIND == kGateUp) {
-    const int unit = n0 + wave * 32;
-    for (int it = 0; it < st.nrb * 2; ++it) {
-      const int r = it * 16 + (lane >> 2), j = lane & 3;
-      const int pr = r ^ (((r >> 2) & 1) << 1);
-      const uint4 v = *(const uint4 *)(ep + pr * 64 + j * 16);
-      const int p = row_begin + r;
-      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * f + unit + j * 8) = v;
-    }
-  } else {
-    const int col0 = n0 + wave * 64;
-    for (int it = 0; it < st.nrb * 4; ++it) {
-      const int r = it * 8 + (lane >> 3), j = lane & 7;
-      const uint4 v = *(const uint4 *)(ep + r * 128 + ((j ^ (((r >> 2) & 1) * 4)) << 4));
-      const int p = row_begin + r;
-      if (p < row_end) *(uint4 *)(out_bf16 + (size_t)p * d + col0 + j * 8) = v;
-    }
-  }
+  store_block<KIND>(acc, st.nrb, KIND == kGateUp ? n0 + wave * 32 : n0 + wave * 64, shared,
+                    row_begin, row_end, TK, d, f, ep, out_bf16, out_f32);
 }
 
 static long long round_up8(long long n) { return (n + kXcds - 1) / kXcds * kXcds; }
