@@ -91,12 +91,16 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   }
   // the top-k once per workgroup (wavefront 0; the other three wait at the
   // barrier instead of repeating it), shared through LDS
+  // A workgroup of slot j needs only the first j + 1 selection rounds; the
+  // first workgroup of the last routed slot takes all k and writes the
+  // token's ids and weights.
   if (wave == 0 && !shared) {
     int id;
     float l;
-    wave_topk<kMaxPerLane>(logits, E, k, &id, &l);
+    const bool writer = slot == k - 1 && n == 0;
+    wave_topk<kMaxPerLane>(logits, E, writer ? k : slot + 1, &id, &l);
     if (lane == slot) s_expert = id;
-    if (gw == 0) {
+    if (writer) {
       const float m = __shfl(l, 0, kWave);
       const float e = lane < k ? expf(l - m) : 0.f;
       const float sum = wave_sum(e);
