@@ -3,11 +3,11 @@
 // weight reuse, so memory bandwidth sets the ceiling).
 //
 // Two kernels, no permutation and no GEMM tiles:
-//   decode_gate_up  every workgroup recomputes the top-k of the token's
-//                   logits on chip (one wavefront, 256 logits) and streams
-//                   gate/up rows of the k routed experts and the shared one
-//                   with 16-byte loads per lane (32 codes), dequantises
-//                   them exactly like the GEMM tiles, and writes
+//   decode_gate_up  every workgroup stages x in LDS, recomputes the top-k of
+//                   the token's logits on chip (one wavefront, 256 logits)
+//                   and streams gate/up rows of the k routed experts and the
+//                   shared one with 16-byte loads per lane (32 codes),
+//                   dequantises them exactly like the GEMM tiles, and writes
 //                   h = bf16(silu(gate) * up) for (k+1) x f units;
 //   decode_down     one wavefront per expert slot streams that slot's down
 //                   rows (16 lanes x 16 bytes per row at f = 512) with its
@@ -35,6 +35,10 @@ __device__ __forceinline__ float dot8(uint4 w, uint4 x, float acc) {
 // wavefronts per workgroup of decode_gate_up; the workgroup's units (4 or 8)
 // belong to one slot (f % 64 == 0)
 constexpr int kDecWaves = 4;
+// columns of x a decode_gate_up workgroup stages in LDS: each lane's first
+// 32 (64 lanes x 32)
+constexpr int kDecXCols = kWave * 32;
+static_assert(kDecWaves * kWave * 8 == kDecXCols, "the workgroup's lanes stage the columns, 8 each");
 // tokens up to which decode_gate_up takes one unit per wavefront (two above)
 constexpr int kDecOneUnitMaxT = 4;
 // wavefronts of a decode_down_slots workgroup at most (one per expert slot)
@@ -63,6 +67,7 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
     int f, int E, int k, int32_t *__restrict__ ids_out, float *__restrict__ wts_out,
     uint16_t *__restrict__ h) {
   __shared__ int s_expert;
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kDecXCols];
   // token blockIdx.y (a few tokens take the same kernels, one grid row each)
   {
     const int t = blockIdx.y;
@@ -80,14 +85,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   const int item = gw * U;
   const int slot = item / f, n = item % f;
   const bool shared = slot == k;
-  // this lane's first 32 columns of x, loaded before the routing (independent of it)
-  uint4 xv0[4] = {};
-  if (lane * 32 < d) {
-    const uint4 *xp = (const uint4 *)(x + lane * 32);
-    xv0[0] = xp[0];
-    xv0[1] = xp[1];
-    xv0[2] = xp[2];
-    xv0[3] = xp[3];
+  // x's first kDecXCols columns, staged in LDS once per workgroup before the
+  // routing (independent of it): each wavefront loads a quarter, 16 bytes per
+  // lane, instead of every wavefront loading all of them from the caches
+  {
+    const int c = (wave * kWave + lane) * 8;
+    if (c < d && c < kDecXCols) *(uint4 *)(s_x + c) = *(const uint4 *)(x + c);
   }
   // the top-k once per workgroup (wavefront 0; the other three wait at the
   // barrier instead of repeating it), shared through LDS
@@ -111,6 +114,15 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
     }
   }
   __syncthreads();
+  // this lane's first 32 columns of x (lane * 32 < kDecXCols always)
+  uint4 xv0[4] = {};
+  if (lane * 32 < d) {
+    const uint4 *xp = (const uint4 *)(s_x + lane * 32);
+    xv0[0] = xp[0];
+    xv0[1] = xp[1];
+    xv0[2] = xp[2];
+    xv0[3] = xp[3];
+  }
   const int expert = shared ? 0 : __builtin_amdgcn_readfirstlane(s_expert);
   const W4 W = shared ? s13 : w13;
   const size_t rb = (size_t)expert * 2 * f;
