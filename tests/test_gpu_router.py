@@ -27,6 +27,11 @@ CASES = [
     G.small_config("rt_t65_d6144_e100", T=65, d=6144, f=64, E=100, k=4, seed=55),
     # 10 K steps: one whole round of eight in flight plus a ragged round
     G.small_config("rt_t64_d640_e64", T=64, d=640, f=64, E=64, k=8, seed=56),
+    # an expert count that is not a multiple of 4 (the scores' row tails)
+    G.small_config("rt_t70_d320_e37", T=70, d=320, f=64, E=37, k=5, seed=59),
+    # a hidden size past the layer's limit (the router projection takes any
+    # multiple of 64): 129 K steps, an odd count split over the two K halves
+    G.small_config("rt_t33_d8256_e24", T=33, d=8256, f=64, E=24, k=4, seed=60),
     G.small_config("rt_t4096_d2048_e256", T=4096, d=2048, f=512, E=256, k=8, seed=57),
 ]
 
