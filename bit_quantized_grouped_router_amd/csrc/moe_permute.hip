@@ -256,12 +256,17 @@ __global__ __launch_bounds__(kPlaceThreads) void perm_place_kernel(
 }
 
 // ------------------------------------------------------------------ small batches
-// Up to kSmallT tokens, routing and permutation take one workgroup and one
-// launch: wavefront w selects the top-k of tokens w, w + 16, w + 32 and
-// w + 48 (all their logits loaded before the first selection), the
-// histogram is counted in LDS, then the scan, tile map and schedule and the
-// stable scatter follow as in the two-kernel path (all tokens form a single
-// token block). Same outputs, bit for bit, as moe_route then moe_permute.
+// Up to kSmallT tokens the permutation takes one workgroup: the histogram is
+// counted in LDS, then the scan, tile map and schedule and the stable scatter
+// follow as in the two-kernel path (all tokens form a single token block).
+// With little selection work the same workgroup also does the routing, so
+// routing and permutation are one launch: wavefront w selects the top-k of
+// tokens w, w + 16, w + 32 and w + 48 (all their logits loaded before the
+// first selection). With more selection work (kMaxPerLane == 0) the route
+// kernel selects first, one wavefront per token over many CUs, and this
+// kernel reads its ids: the sixteen wavefronts of one workgroup would run
+// their tokens' k selection rounds one after another. Same outputs, bit for bit,
+// as moe_route then moe_permute, either way.
 constexpr int kSmallT = 64;
 constexpr int kSmallPerWave = kSmallT / (kPlaceThreads / kWave);  // 4
 
@@ -277,29 +282,40 @@ __global__ __launch_bounds__(kPlaceThreads) void route_permute_small_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   for (int i = tid; i < E; i += kPlaceThreads) cnt[i] = 0;
-  float v[kSmallPerWave][kMaxPerLane];
-#pragma unroll
-  for (int i = 0; i < kSmallPerWave; ++i) {
-    const int t = wave + 16 * i;
-    wave_load_logits<kMaxPerLane>(logits + (size_t)(t < T ? t : T - 1) * E, E, v[i]);
-  }
-  __syncthreads();
-  // ---- top-k and router weights (the same arithmetic as the route kernel)
-#pragma unroll
-  for (int i = 0; i < kSmallPerWave; ++i) {
-    const int t = wave + 16 * i;
-    if (t >= T) break;  // wave-uniform
-    int id;
-    float l;
-    wave_topk_loaded<kMaxPerLane>(v[i], E, k, &id, &l);
-    const float m = __shfl(l, 0, kWave);
-    const float e = lane < k ? expf(l - m) : 0.f;
-    const float sum = wave_sum(e);
-    if (lane < k) {
-      ids_out[(size_t)t * k + lane] = id;
-      wts_out[(size_t)t * k + lane] = e / sum;
-      ids_s[t * k + lane] = id;
+  if constexpr (kMaxPerLane == 0) {
+    // ---- the route kernel's ids (in range for any input), counted in LDS
+    __syncthreads();
+    for (int a = tid; a < T * k; a += kPlaceThreads) {
+      const int id = clamp_id(ids_out[a], E);
+      ids_s[a] = id;
       atomicAdd(&cnt[id], 1);
+    }
+  } else {
+    constexpr int kM = kMaxPerLane > 0 ? kMaxPerLane : 1;
+    float v[kSmallPerWave][kM];
+#pragma unroll
+    for (int i = 0; i < kSmallPerWave; ++i) {
+      const int t = wave + 16 * i;
+      wave_load_logits<kM>(logits + (size_t)(t < T ? t : T - 1) * E, E, v[i]);
+    }
+    __syncthreads();
+    // ---- top-k and router weights (the same arithmetic as the route kernel)
+#pragma unroll
+    for (int i = 0; i < kSmallPerWave; ++i) {
+      const int t = wave + 16 * i;
+      if (t >= T) break;  // wave-uniform
+      int id;
+      float l;
+      wave_topk_loaded<kM>(v[i], E, k, &id, &l);
+      const float m = __shfl(l, 0, kWave);
+      const float e = lane < k ? expf(l - m) : 0.f;
+      const float sum = wave_sum(e);
+      if (lane < k) {
+        ids_out[(size_t)t * k + lane] = id;
+        wts_out[(size_t)t * k + lane] = e / sum;
+        ids_s[t * k + lane] = id;
+        atomicAdd(&cnt[id], 1);
+      }
     }
   }
   __syncthreads();
@@ -393,6 +409,17 @@ hipError_t launch_route_permute(const Dims &dm, const float *logits, int32_t *id
     if (const hipError_t e = launch_route(logits, dm.T, dm.E, dm.k, ids, wts, s)) return e;
     return launch_permute(dm, ids, counts, offsets, sorted_token, row_of, tile_map, num_tiles,
                           block_counts, s);
+  }
+  // selection rounds per wavefront in the one-launch kernel, weighted 4x for
+  // the general selection (more than 256 experts); measured on gfx950, one
+  // launch is faster up to about 16 (T = 32 at k = 8)
+  const int rounds = (dm.T + 15) / 16 * dm.k * (dm.E > 256 ? 4 : 1);
+  if (rounds > 16) {
+    if (const hipError_t e = launch_route(logits, dm.T, dm.E, dm.k, ids, wts, s)) return e;
+    route_permute_small_kernel<0><<<1, kPlaceThreads, 0, s>>>(
+        logits, dm.T, dm.E, dm.k, ids, wts, counts, offsets, sorted_token, row_of, tile_map,
+        num_tiles);
+    return hipGetLastError();
   }
   if (dm.E <= 64)
     route_permute_small_kernel<1><<<1, kPlaceThreads, 0, s>>>(

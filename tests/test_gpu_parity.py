@@ -115,11 +115,17 @@ def test_route_permute_bit_exact(cfg):
     assert np.array_equal(p["tile_map"][:n, 3], expected_schedule(ref["tiles"]))
 
 
+# Up to 64 tokens: one launch when each of the workgroup's wavefronts has at
+# most 16 selection rounds (general selection above 256 experts counted 4x),
+# else the route kernel and then the one-workgroup permutation.
 ROUTE_PERMUTE = [
-    G.small_config("rp_t1", T=1, d=64, f=64, E=256, k=8, seed=71),
-    G.small_config("rp_t2", T=2, d=64, f=64, E=256, k=8, seed=72),
-    G.small_config("rp_t37_e5", T=37, d=64, f=64, E=5, k=3, seed=73),
-    G.small_config("rp_t64_kE", T=64, d=64, f=64, E=8, k=8, seed=74),
+    G.small_config("rp_t1", T=1, d=64, f=64, E=256, k=8, seed=71),       # one launch
+    G.small_config("rp_t2", T=2, d=64, f=64, E=256, k=8, seed=72),       # one launch
+    G.small_config("rp_t32", T=32, d=64, f=64, E=256, k=8, seed=79),     # one launch, 16 rounds
+    G.small_config("rp_t33", T=33, d=64, f=64, E=256, k=8, seed=80),     # route + permutation
+    G.small_config("rp_t37_e5", T=37, d=64, f=64, E=5, k=3, seed=73),    # one launch
+    G.small_config("rp_t16_e1000_k4", T=16, d=64, f=64, E=1000, k=4, seed=95),  # one launch
+    G.small_config("rp_t64_kE", T=64, d=64, f=64, E=8, k=8, seed=74),    # route + permutation
     G.small_config("rp_t64_e1000", T=64, d=64, f=64, E=1000, k=32, seed=75),
     G.small_config("rp_t50_zipf_empty", T=50, d=64, f=64, E=256, k=8, seed=76, zipf_s=1.1,
                    n_forced_empty=8),
@@ -130,8 +136,8 @@ ROUTE_PERMUTE = [
 
 @pytest.mark.parametrize("cfg", ROUTE_PERMUTE, ids=lambda c: c.name)
 def test_route_permute_one_call(cfg):
-    """moe_route_permute (one workgroup up to 64 tokens) against the oracle, bit for bit,
-    and against moe_route followed by moe_permute."""
+    """moe_route_permute (its one-workgroup paths up to 64 tokens) against the oracle, bit
+    for bit, and against moe_route followed by moe_permute."""
     say(f"[route_permute] {cfg.name}")
     a = G.make_activations(cfg)
     logits = torch.from_numpy(a["logits"]).cuda()
