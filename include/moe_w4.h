@@ -170,9 +170,12 @@ moe_status moe_permute(const moe_dims *dm, const int32_t *topk_ids, int32_t *cou
 
 /*
  * moe_route_permute - moe_route followed by moe_permute, with the same
- * outputs bit for bit. Up to 64 tokens it is a single one-workgroup launch
- * (top-k, histogram, scan, block map and scatter together), which removes
- * most of the fixed cost of the routing at small batches.
+ * outputs bit for bit. Up to 64 tokens the permutation is a single
+ * one-workgroup launch (histogram, scan, block map and scatter together),
+ * which removes most of the fixed cost of the routing at small batches; the
+ * top-k runs in the same launch while it is short (at most 16 selection
+ * rounds per wavefront, e.g. up to 32 tokens at k = 8 and E <= 256), and in
+ * the moe_route kernel just before it otherwise.
  *   logits                      fp32 [T][E]
  *   topk_ids, topk_w            out, as moe_route
  *   counts .. num_tiles         out, as moe_permute
