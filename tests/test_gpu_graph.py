@@ -54,6 +54,10 @@ def _setup(cfg):
     # workgroup (T = 12)
     G.small_config("graph_decode_t3", T=3, d=2048, f=512, E=256, k=8, seed=45),
     G.small_config("graph_decode_t12", T=12, d=256, f=128, E=32, k=8, seed=46),
+    # the small-batch routing paths: one launch (T = 24), and the route kernel
+    # before the one-workgroup permutation (T = 48)
+    G.small_config("graph_small_t24", T=24, d=256, f=128, E=64, k=8, seed=47),
+    G.small_config("graph_small_t48", T=48, d=256, f=128, E=64, k=8, seed=48),
 ], ids=lambda c: c.name)
 def test_graph_replays_match_eager(cfg):
     say(f"[graph] {cfg.name}")
