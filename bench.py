@@ -18,8 +18,8 @@ step, inputs resident in HBM. Also reported on the same JSON line:
   mixed_bias    the headline layer with mixed dequantisation biases;
   cpu_baseline  the CPU oracle on the whole headline layer (and, under
                 configs, on the whole layer of each other workload);
-  small_batch   (--small-batch) the layer at T = 1 .. 64, bytes of the used
-                experts' weights / time.
+  small_batch   the layer at T = 1, 2, 8, 32, 64 (skipped with
+                --no-small-batch), bytes of the used experts' weights / time.
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 import argparse
@@ -147,7 +147,10 @@ def main():
     ap.add_argument("--cpu-headline-only", action="store_true",
                     help="time the CPU oracle on the headline layer only")
     ap.add_argument("--small-batch", action="store_true",
-                    help="also time moe_layer_forward at T = 1, 2, 8, 32, 64")
+                    help="time moe_layer_forward at T = 1, 2, 8, 32, 64 (the default; kept "
+                         "for older command lines)")
+    ap.add_argument("--no-small-batch", action="store_true",
+                    help="skip the small-batch timings")
     ap.add_argument("--calibrate-copy", action="store_true",
                     help="also run one plain 256 MiB device-to-device copy (a reference "
                          "kernel of known traffic for hardware byte counters)")
@@ -344,7 +347,7 @@ def main():
     # moe_layer_forward at T = 1 .. 64 (the general path; T = 1 takes the
     # decode kernels), two weight copies alternated, events around 100 calls
     small = None
-    if args.small_batch:
+    if not args.no_small_batch:
         log("[bench] small batches")
         w2 = M.W4Weights.from_numpy(weights_np, device=dev)
         wcs = [wc, w2.c()]
