@@ -156,8 +156,8 @@ def main():
                          "kernel of known traffic for hardware byte counters)")
     args = ap.parse_args()
     if args.gpus != 1:
-        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported by this "
-              "build (no multi-GPU path)", file=sys.stderr)
+        print(f"bench.py runs on exactly one GPU; --gpus {args.gpus} is not supported (the "
+              "layer has no multi-GPU path)", file=sys.stderr)
         sys.exit(2)
 
     import numpy as np
