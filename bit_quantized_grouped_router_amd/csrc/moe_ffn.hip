@@ -44,15 +44,23 @@ constexpr int kThreads = kWaves * 64;
 constexpr int kWgCols = 64 * kWaves;         // weight rows per workgroup (64 per wavefront)
 constexpr int kRB = kBlockM / 32;            // 32-row blocks per tile
 constexpr int kStages = 3;                   // activation ring depth
-constexpr int kStageBytes = kBlockM * 128;   // one K step of the tile's rows, bf16
-constexpr int kDma = kBlockM * 8 / kThreads;  // 16-byte DMA chunks per thread per K step
 constexpr int kDmaRows = kThreads / 8;        // tile rows one DMA instruction of the workgroup fills
-static_assert(kWaves % 2 == 0 && kBlockM % kDmaRows == 0, "DMA row mapping");
+static_assert(kWaves % 2 == 0 && kBlockM % kDmaRows == 0 && kDmaRows == 32, "DMA row mapping");
 constexpr int kXcds = 8;
 
+// The kernel is compiled twice: for tiles of up to MRB = kRB row blocks (the
+// block map's full tiles), and for MRB = 1, used when no tile of the launch
+// can have more than 32 rows (small batches). The second needs a quarter of
+// the accumulators and of the activation ring, so more workgroups share a CU
+// and hide one another's latencies; per row block it runs the same
+// instructions, so its results are the same bits.
+constexpr int kShortOcc = 3;  // workgroups per CU of the MRB = 1 kernel
+template <int MRB>
+constexpr int stage_bytes() { return MRB * 32 * 128; }  // one K step of the tile's rows, bf16
 // workgroups per CU the register budget is sized for (128-row tiles leave
 // room for two; 256-row tiles need all 512 registers of a lane)
-constexpr int kOcc = kBlockM <= 128 && kWaves <= 4 ? 2 : 1;
+template <int MRB>
+constexpr int gemm_occ() { return MRB == 1 ? kShortOcc : (MRB <= 4 && kWaves <= 4 ? 2 : 1); }
 
 enum { kGateUp = 0, kDown = 1 };
 
@@ -85,11 +93,11 @@ typedef uint32_t u32x4_t __attribute__((ext_vector_type(4)));
 // through a buffer resource (byte offsets: a_off, plus the step as a scalar).
 // DMA instruction i fills 32-row block i of the tile, so a tile with NRB
 // active row blocks issues the first NRB.
-template <int NRB>
+template <int NRB, int MRB>
 __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t actr,
-                                          const uint32_t (&a_off)[kDma], uint8_t *lds,
+                                          const uint32_t *a_off, uint8_t *lds,
                                           uint32_t a_lds, int src, int stage) {
-  uint8_t *s = lds + stage * kStageBytes + a_lds;
+  uint8_t *s = lds + stage * stage_bytes<MRB>() + a_lds;
 #pragma unroll
   for (int i = 0; i < NRB; ++i)
     __builtin_amdgcn_raw_ptr_buffer_load_lds(actr, (lds_void *)(s + i * kDmaRows * 128), 16, a_off[i],
@@ -97,10 +105,11 @@ __device__ __forceinline__ void dma_stage(__amdgpu_buffer_rsrc_t actr,
 }
 
 // Per-workgroup state of one tile, set up once before the K loop.
+template <int MRB>
 struct TileSetup {
   __amdgpu_buffer_rsrc_t actr;       // activation matrix (x for gate/up, h for down)
   __amdgpu_buffer_rsrc_t actr_none;  // the same with no records: every access out of range
-  uint32_t a_off[kDma];   // byte offsets (K step 0) of this lane's DMA chunks
+  uint32_t a_off[MRB];    // byte offsets (K step 0) of this lane's DMA chunks (one per row block)
   uint32_t a_lds;         // LDS byte offset of this wavefront's first DMA slot in a stage
   __amdgpu_buffer_rsrc_t codes;       // the expert's codes
   __amdgpu_buffer_rsrc_t codes_none;  // the same with no records
@@ -108,7 +117,7 @@ struct TileSetup {
   const uint32_t *sbl;    // LDS table [K/64][256] of (scale | bias << 16) per weight row
   int lr0;                // this lane's table column for block 0 (block 1 adds 32)
   int ksteps;
-  int nrb;                // active 32-row blocks of the tile (1..kRB), wave-uniform
+  int nrb;                // active 32-row blocks of the tile (1..MRB), wave-uniform
 };
 
 // Schedule check build (MOE_SCHED_CHECK=1, a separate library made by the
@@ -125,7 +134,7 @@ struct TileSetup {
   } while (0)
 #endif
 
-// K loop of one tile. NRB: the tile's active 32-row blocks (1..kRB), known
+// K loop of one tile. NRB: the tile's active 32-row blocks (1..MRB), known
 // at compile time, so a short tile moves, reads and multiplies only the rows
 // it has (the activation DMA, the A-fragment reads and the MFMAs all scale
 // with NRB; the dequantisation does not). FAST: every group of this
@@ -140,9 +149,9 @@ struct TileSetup {
 // slice's fragment reads in flight past the end of a step), DMA of stage
 // kt+2 into the slot of stage kt-1, code loads for step kt+2, then the four
 // K slices.
-template <int NRB, bool FAST>
-__device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
-                                            f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
+template <int NRB, bool FAST, int MRB>
+__device__ __forceinline__ void gemm_k_loop(const TileSetup<MRB> &st, uint8_t *lds,
+                                            f32x16_t (&acc)[MRB][2], const u32x4_t (&cr0)[2],
                                             const u32x4_t (&cr1)[2]) {
   const int lane = threadIdx.x & 63;
   const int klast = st.ksteps - 1;
@@ -164,8 +173,10 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
   // stay in the instruction stream (so every wait count holds) but touch no
   // memory and return zeros into a stage or code slot no one reads
 #define MOE_DMA(src_, stage_)                                                                \
-  dma_stage<NRB>((src_) <= klast ? st.actr : st.actr_none, st.a_off, lds, st.a_lds,          \
-            (src_) <= klast ? (src_) : 0, (stage_))
+  {                                                                                          \
+    const __amdgpu_buffer_rsrc_t r_ = (src_) <= klast ? st.actr : st.actr_none;             \
+    dma_stage<NRB, MRB>(r_, st.a_off, lds, st.a_lds, (src_) <= klast ? (src_) : 0, (stage_)); \
+  }
 #define MOE_LOAD_B(kt_, slot_)                                                              \
   {                                                                                         \
     const __amdgpu_buffer_rsrc_t r_ = (kt_) <= klast ? st.codes : st.codes_none;             \
@@ -215,7 +226,7 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
       sb0 = st.sbl[kn_];                                                                     \
       sb1 = st.sbl[kn_ + 32];                                                                \
     }                                                                                        \
-    const uint8_t *abuf_ = lds + (ktv_ % kStages) * kStageBytes;                             \
+    const uint8_t *abuf_ = lds + (ktv_ % kStages) * stage_bytes<MRB>();                      \
     const DqGroup q0_ = dq_consts(s0_), q1_ = dq_consts(s1_);                                \
     _Pragma("unroll") for (int ks = 0; ks < 4; ++ks) {                                       \
       const uint8_t *aks_ = abuf_ + lrow + (((lh + ks) ^ lx) << 4);                          \
@@ -267,18 +278,18 @@ __device__ __forceinline__ void gemm_k_loop(const TileSetup &st, uint8_t *lds,
 }
 
 // DMA of ring stages 0 and 1 (K steps 0 and 1) for a tile of NRB row blocks.
-template <int NRB>
-__device__ __forceinline__ void prologue_dma(const TileSetup &st, uint8_t *lds, int klast) {
-  dma_stage<NRB>(st.actr, st.a_off, lds, st.a_lds, 0, 0);
-  dma_stage<NRB>(st.actr, st.a_off, lds, st.a_lds, min(1, klast), 1);
+template <int NRB, int MRB>
+__device__ __forceinline__ void prologue_dma(const TileSetup<MRB> &st, uint8_t *lds, int klast) {
+  dma_stage<NRB, MRB>(st.actr, st.a_off, lds, st.a_lds, 0, 0);
+  dma_stage<NRB, MRB>(st.actr, st.a_off, lds, st.a_lds, min(1, klast), 1);
 }
 
 // The K loop for a tile of NRB row blocks, entered once stage 0 has landed
 // (only the NRB chunks of stage 1 may still be in flight, so the loop's
 // first wait holds at once).
-template <int NRB>
-__device__ __forceinline__ void tile_k_loop(const TileSetup &st, uint8_t *lds,
-                                            f32x16_t (&acc)[kRB][2], const u32x4_t (&cr0)[2],
+template <int NRB, int MRB>
+__device__ __forceinline__ void tile_k_loop(const TileSetup<MRB> &st, uint8_t *lds,
+                                            f32x16_t (&acc)[MRB][2], const u32x4_t (&cr0)[2],
                                             const u32x4_t (&cr1)[2], bool fast) {
   MOE_WAIT_VMCNT(NRB);
   if (fast)
@@ -294,8 +305,8 @@ __device__ __forceinline__ void tile_k_loop(const TileSetup &st, uint8_t *lds,
 // outputs go through the LDS region ep as [row][col] tiles and leave as
 // 16-byte row chunks; the shared expert's fp32 down outputs are stored
 // directly.
-template <int KIND>
-__device__ __forceinline__ void store_block(const f32x16_t (&acc)[kRB][2], int nrb, int colbase,
+template <int KIND, int MRB>
+__device__ __forceinline__ void store_block(const f32x16_t (&acc)[MRB][2], int nrb, int colbase,
                                             bool shared, int row_begin, int row_end, int TK,
                                             int d, int f, uint8_t *ep, uint16_t *out_bf16,
                                             float *out_f32) {
@@ -307,7 +318,7 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[kRB][2], int n
     // fp32 rows of the shared expert: 128 contiguous bytes per half-wavefront
     const int wrow0 = colbase + c, wrow1 = colbase + 32 + c;
 #pragma unroll
-    for (int rb = 0; rb < kRB; ++rb) {
+    for (int rb = 0; rb < MRB; ++rb) {
       if (rb >= nrb) continue;
 #pragma unroll
       for (int r = 0; r < 16; ++r) {
@@ -324,7 +335,7 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[kRB][2], int n
   // (4 * ((r / 4) % 2)). Either way the two halves of the wavefront (rows r
   // and r + 4) write disjoint banks.
 #pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) {
+  for (int rb = 0; rb < MRB; ++rb) {
     if (rb >= nrb) continue;
 #pragma unroll
     for (int r = 0; r < 16; r += 2) {
@@ -365,16 +376,17 @@ __device__ __forceinline__ void store_block(const f32x16_t (&acc)[kRB][2], int n
   }
 }
 
-template <int KIND>
-__global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
+template <int KIND, int MRB>
+__global__ __launch_bounds__(kThreads, gemm_occ<MRB>()) void grouped_gemm_w4_kernel(
     const uint16_t *__restrict__ act, W4 wr, W4 ws, const int32_t *__restrict__ sorted_token,
     const int32_t *__restrict__ tile_map, const int32_t *__restrict__ num_tiles_p,
     uint16_t *__restrict__ out_bf16, float *__restrict__ out_f32, int T, int d, int f, int E,
     int k) {
   // LDS: the activation ring, then the scale/bias table of the tile's 256
-  // weight rows for all K/64 groups (sized by the launch)
+  // weight rows for all K/64 groups (sized by the launch), then (MRB = 1
+  // down only) the output staging
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  uint32_t *sbl = (uint32_t *)(smem + kStages * kStageBytes);
+  uint32_t *sbl = (uint32_t *)(smem + kStages * stage_bytes<MRB>());
 
   // K: input width of the GEMM
   const int K = KIND == kGateUp ? d : f;
@@ -395,7 +407,7 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
   const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // wave-uniform, in a scalar register
   const int TK = T * k;
 
-  TileSetup st;
+  TileSetup<MRB> st;
   {
     // x: T rows of d; h: T*k routed + T shared rows of f (under 2^32 bytes)
     const uint32_t act_bytes =
@@ -405,30 +417,14 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
   }
   st.ksteps = K / kKT;
   const int klast = st.ksteps - 1;
-  // the tile's active 32-row blocks (the same for every wavefront: the DMA
-  // fills each row block with all four), clamped to 1..kRB for any map
+  // The tile's 32-row blocks (clamped to 1..kRB for any map), taken MRB at a
+  // time: the full-tile kernel makes one pass, the MRB = 1 kernel one pass
+  // per block (each rebuilding the weights; it is launched for small batches,
+  // where nearly every tile has a single block). Passes after the first reuse
+  // the scale table.
   const int rows = row_end - row_begin;
-  const int tile_rb = min(max((rows + 31) / 32, 1), kRB);
-  // ---- prologue. The loads go out in dependency order so that their
-  // latencies overlap: token indices (they gate the activation DMA), codes of
-  // steps 0 and 1 and the tile's scales (they need only the tile), then the
-  // DMA of stages 0 and 1; the scale table is written while the DMA is in
-  // flight.
-  //
-  // Activation rows: DMA instruction i of wavefront w fills tile rows
-  // R i + 8 w .. +7, R = 8 x wavefronts (1 KB, 16 bytes per lane in lane
-  // order); lane l lands in row r = R i + 8 w + l / 8 at 16-byte slot l % 8,
-  // which holds logical chunk (l % 8) ^ (r % 8) ^ ((r / 8) % 2) of the row
-  // (the swizzle; (r / 8) % 2 == w % 2 as R / 8 is even). Rows
-  // past the tile's end re-read its last row (their results are never
-  // stored), so every load is unconditional.
-  st.a_lds = (uint32_t)wave * 1024u;
-  int tok[kDma];
-#pragma unroll
-  for (int i = 0; i < kDma; ++i) {
-    const int p = min(row_begin + kDmaRows * i + 8 * wave + (lane >> 3), row_end - 1);
-    tok[i] = KIND == kGateUp ? (shared ? p - TK : sorted_token[p]) : p;
-  }
+  const int tile_blocks = min(max((rows + 31) / 32, 1), kRB);
+  const int npass = MRB == kRB ? 1 : tile_blocks;
   // ---- this wavefront's two 32-row blocks of weight rows
   bool wave_on;  // wave-uniform: this wavefront has weight rows (both blocks: f, d % 64 == 0)
   int wrow0, wrow1;
@@ -450,127 +446,202 @@ __global__ __launch_bounds__(kThreads, kOcc) void grouped_gemm_w4_kernel(
   st.codes_none = __builtin_amdgcn_make_buffer_rsrc((void *)W.codes, (short)0, 0, 0x00020000);
   st.c_off[0] = R0 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
   st.c_off[1] = R1 * (uint32_t)(K / 2) + (uint32_t)(lane >> 5) * 16u;
-  u32x4_t cr0[2], cr1[2];
-#pragma unroll
-  for (int b = 0; b < 2; ++b) {
-    cr0[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(st.codes, st.c_off[b], 0, 0));
-    cr1[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
-                                             st.codes, st.c_off[b], min(1, klast) * (kKT / 2), 0));
-  }
-  // the scale/bias table: lane l of wavefront w fills column 64 w + l, which
-  // is weight row R0 (l < 32) or R1 (l >= 32) of lane l % 32, for all groups;
-  // the wavefront reads back only its own columns. The same pass decides
-  // whether all of them allow the fast dequantisation. Groups are taken 32 at
-  // a time with all their loads issued together.
   st.sbl = sbl;
   st.lr0 = wave * 64 + (lane & 31);
-  const int ng = K / kGroup;
-  const size_t srow = (ex * (size_t)nrows_w + ((lane >> 5) ? R1 : R0)) * (size_t)ng;
-  const uint16_t *sp = W.scales + srow, *bp = W.biases + srow;
-  uint32_t *col = sbl + wave * 64 + lane;
-  bool fast_ok = true;
-  const bool vec = ng % 8 == 0;  // rows start 16-byte aligned: 16-byte loads
-  uint4 sv[4], bv[4];
-  if (vec) {
+  st.a_lds = (uint32_t)wave * 1024u;
+  // output staging, per wavefront: inside the ring for the full-tile kernel
+  // and for MRB = 1 gate/up (8 KB), after the scale table for MRB = 1 down,
+  // whose 16 KB would reach into the table that later passes reuse
+  static_assert(kWaves * 32 * 64 <= kStages * stage_bytes<1>(), "gate/up staging fits in the ring");
+  uint8_t *const ep_base =
+      smem + (MRB == 1 && KIND == kDown
+                  ? kStages * stage_bytes<MRB>() + (K / kGroup) * kWgCols * 4 : 0);
+  bool fast = true;
+
+  // one pass over rows pr_begin .. pr_end - 1; FIRST: the pass that loads
+  // the scale table
+  auto run_pass = [&](auto first_tag, const int pr_begin, const int pr_end) {
+    constexpr bool FIRST = decltype(first_tag)::value;
+    // the pass's active 32-row blocks (the same for every wavefront: the DMA
+    // fills each row block with all four)
+    const int tile_rb = MRB == 1 ? 1 : tile_blocks;
+    // ---- prologue. The loads go out in dependency order so that their
+    // latencies overlap: token indices (they gate the activation DMA), codes
+    // of steps 0 and 1 and (first pass) the tile's scales (they need only the
+    // tile), then the DMA of stages 0 and 1; the scale table is written while
+    // the DMA is in flight.
+    //
+    // Activation rows: DMA instruction i of wavefront w fills rows
+    // R i + 8 w .. +7 of the pass, R = 8 x wavefronts (1 KB, 16 bytes per
+    // lane in lane order); lane l lands in row r = R i + 8 w + l / 8 at
+    // 16-byte slot l % 8, which holds logical chunk (l % 8) ^ (r % 8) ^
+    // ((r / 8) % 2) of the row (the swizzle; (r / 8) % 2 == w % 2 as R / 8 is
+    // even). Rows past the pass's end re-read its last row (their results
+    // are never stored), so every load is unconditional.
+    int tok[MRB];
 #pragma unroll
-    for (int q = 0; q < 4; ++q) {
-      const int g0 = min(8 * q, ng - 8);
-      sv[q] = *(const uint4 *)(sp + g0);
-      bv[q] = *(const uint4 *)(bp + g0);
+    for (int i = 0; i < MRB; ++i) {
+      const int p = min(pr_begin + kDmaRows * i + 8 * wave + (lane >> 3), pr_end - 1);
+      tok[i] = KIND == kGateUp ? (shared ? p - TK : sorted_token[p]) : p;
     }
-  }
-  // token rows -> activation offsets, then the DMA of stages 0 and 1
-  {
-    const uint32_t j = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
+    u32x4_t cr0[2], cr1[2];
 #pragma unroll
-    for (int i = 0; i < kDma; ++i) {
-      const int t = KIND == kGateUp ? (tok[i] < 0 ? 0 : (tok[i] >= T ? T - 1 : tok[i])) : tok[i];
-      st.a_off[i] = ((uint32_t)t * (uint32_t)K + j * 8u) * 2u;  // token clamped: in range for any routing
+    for (int b = 0; b < 2; ++b) {
+      cr0[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(st.codes, st.c_off[b], 0, 0));
+      cr1[b] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(
+                                               st.codes, st.c_off[b], min(1, klast) * (kKT / 2), 0));
     }
-  }
-  // the DMA of stages 0 and 1
-  switch (tile_rb) {
-    case 1: prologue_dma<1>(st, smem, klast); break;
-    case 2: prologue_dma<2>(st, smem, klast); break;
-    case 3: prologue_dma<3>(st, smem, klast); break;
-    default: prologue_dma<kRB>(st, smem, klast); break;
-  }
-  if (vec) {
-    for (int g0 = 0; g0 < ng; g0 += 32) {
-      if (g0 > 0) {
-#pragma unroll
-        for (int q = 0; q < 4; ++q) {
-          const int g1 = min(g0 + 8 * q, ng - 8);
-          sv[q] = *(const uint4 *)(sp + g1);
-          bv[q] = *(const uint4 *)(bp + g1);
-        }
-      }
+    // the scale/bias table (first pass): lane l of wavefront w fills column
+    // 64 w + l, which is weight row R0 (l < 32) or R1 (l >= 32) of lane l %
+    // 32, for all groups; the wavefront reads back only its own columns. The
+    // same pass decides whether all of them allow the fast dequantisation.
+    // Groups are taken 32 at a time with all their loads issued together.
+    const int ng = K / kGroup;
+    const size_t srow = (ex * (size_t)nrows_w + ((lane >> 5) ? R1 : R0)) * (size_t)ng;
+    const uint16_t *sp = W.scales + srow, *bp = W.biases + srow;
+    uint32_t *col = sbl + wave * 64 + lane;
+    const bool vec = ng % 8 == 0;  // rows start 16-byte aligned: 16-byte loads
+    uint4 sv[4], bv[4];
+    if (FIRST && vec) {
 #pragma unroll
       for (int q = 0; q < 4; ++q) {
-        if (g0 + 8 * q >= ng) break;
-        const uint32_t su[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
-        const uint32_t bu[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
-#pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          const uint32_t w0 = (su[e] & 0xFFFFu) | (bu[e] << 16);
-          const uint32_t w1 = (su[e] >> 16) | (bu[e] & 0xFFFF0000u);
-          col[(g0 + 8 * q + 2 * e) * kWgCols] = w0;
-          col[(g0 + 8 * q + 2 * e + 1) * kWgCols] = w1;
-          fast_ok &= (int)dq_fast_ok(w0) & (int)dq_fast_ok(w1);
-        }
+        const int g0 = min(8 * q, ng - 8);
+        sv[q] = *(const uint4 *)(sp + g0);
+        bv[q] = *(const uint4 *)(bp + g0);
       }
     }
-  } else {
-    for (int g0 = 0; g0 < ng; ++g0) {
-      const uint32_t w0 = (uint32_t)sp[g0] | ((uint32_t)bp[g0] << 16);
-      col[g0 * kWgCols] = w0;
-      fast_ok &= dq_fast_ok(w0);
+    // token rows -> activation offsets, then the DMA of stages 0 and 1
+    {
+      const uint32_t j = (uint32_t)((lane & 7) ^ (lane >> 3) ^ (wave & 1));
+#pragma unroll
+      for (int i = 0; i < MRB; ++i) {
+        const int t = KIND == kGateUp ? (tok[i] < 0 ? 0 : (tok[i] >= T ? T - 1 : tok[i])) : tok[i];
+        st.a_off[i] = ((uint32_t)t * (uint32_t)K + j * 8u) * 2u;  // token clamped: in range for any routing
+      }
+    }
+    // a later pass's DMA refills LDS that the previous pass's epilogue read
+    if (!FIRST) lds_barrier();
+    if constexpr (MRB == 1) {
+      prologue_dma<1>(st, smem, klast);
+    } else {
+      switch (tile_rb) {
+        case 1: prologue_dma<1>(st, smem, klast); break;
+        case 2: prologue_dma<2>(st, smem, klast); break;
+        case 3: prologue_dma<3>(st, smem, klast); break;
+        default: prologue_dma<MRB>(st, smem, klast); break;
+      }
+    }
+    if (FIRST) {
+      bool fast_ok = true;
+      if (vec) {
+        for (int g0 = 0; g0 < ng; g0 += 32) {
+          if (g0 > 0) {
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+              const int g1 = min(g0 + 8 * q, ng - 8);
+              sv[q] = *(const uint4 *)(sp + g1);
+              bv[q] = *(const uint4 *)(bp + g1);
+            }
+          }
+#pragma unroll
+          for (int q = 0; q < 4; ++q) {
+            if (g0 + 8 * q >= ng) break;
+            const uint32_t su[4] = {sv[q].x, sv[q].y, sv[q].z, sv[q].w};
+            const uint32_t bu[4] = {bv[q].x, bv[q].y, bv[q].z, bv[q].w};
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              const uint32_t w0 = (su[e] & 0xFFFFu) | (bu[e] << 16);
+              const uint32_t w1 = (su[e] >> 16) | (bu[e] & 0xFFFF0000u);
+              col[(g0 + 8 * q + 2 * e) * kWgCols] = w0;
+              col[(g0 + 8 * q + 2 * e + 1) * kWgCols] = w1;
+              fast_ok &= (int)dq_fast_ok(w0) & (int)dq_fast_ok(w1);
+            }
+          }
+        }
+      } else {
+        for (int g0 = 0; g0 < ng; ++g0) {
+          const uint32_t w0 = (uint32_t)sp[g0] | ((uint32_t)bp[g0] << 16);
+          col[g0 * kWgCols] = w0;
+          fast_ok &= dq_fast_ok(w0);
+        }
+      }
+      fast = __builtin_amdgcn_ballot_w64(!fast_ok) == 0;  // wave-uniform
+    }
+    st.nrb = wave_on ? tile_rb : 0;
+
+    f32x16_t acc[MRB][2];
+#pragma unroll
+    for (int rb = 0; rb < MRB; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
+    // a wavefront with no weight rows runs the same loop (its share of the
+    // DMA and the barriers are needed) and stores nothing
+    if constexpr (MRB == 1) {
+      tile_k_loop<1>(st, smem, acc, cr0, cr1, fast);
+    } else {
+      switch (tile_rb) {
+        case 1: tile_k_loop<1>(st, smem, acc, cr0, cr1, fast); break;
+        case 2: tile_k_loop<2>(st, smem, acc, cr0, cr1, fast); break;
+        case 3: tile_k_loop<3>(st, smem, acc, cr0, cr1, fast); break;
+        default: tile_k_loop<MRB>(st, smem, acc, cr0, cr1, fast); break;
+      }
+    }
+
+    // ---- epilogue. Every wavefront's LDS reads of the ring have completed
+    // before any wavefront reuses the LDS.
+    lds_barrier();
+    asm volatile("" ::: "memory");
+    if (wave_on) {
+      uint8_t *ep = ep_base + wave * (KIND == kGateUp ? MRB * 32 * 64 : MRB * 32 * 128);
+      store_block<KIND, MRB>(acc, st.nrb, KIND == kGateUp ? n0 + wave * 32 : n0 + wave * 64,
+                             shared, pr_begin, pr_end, TK, d, f, ep, out_bf16, out_f32);
+    }
+  };
+
+  run_pass(std::true_type{}, row_begin, min(row_end, row_begin + MRB * 32));
+  if constexpr (MRB == 1) {
+    for (int pass = 1; pass < npass; ++pass) {
+      const int pr_begin = row_begin + pass * 32;
+      run_pass(std::false_type{}, pr_begin, min(row_end, pr_begin + 32));
     }
   }
-  const bool fast = __builtin_amdgcn_ballot_w64(!fast_ok) == 0;  // wave-uniform
-  st.nrb = wave_on ? tile_rb : 0;
-
-  f32x16_t acc[kRB][2];
-#pragma unroll
-  for (int rb = 0; rb < kRB; ++rb) acc[rb][0] = acc[rb][1] = f32x16_t{0};
-  // a wavefront with no weight rows runs the same loop (its share of the
-  // DMA and the barriers are needed) and stores nothing
-  switch (tile_rb) {
-    case 1: tile_k_loop<1>(st, smem, acc, cr0, cr1, fast); break;
-    case 2: tile_k_loop<2>(st, smem, acc, cr0, cr1, fast); break;
-    case 3: tile_k_loop<3>(st, smem, acc, cr0, cr1, fast); break;
-    default: tile_k_loop<kRB>(st, smem, acc, cr0, cr1, fast); break;
-  }
-
-  // ---- epilogue. Every wavefront's LDS reads of the ring have completed
-  // before any wavefront reuses the LDS.
-  lds_barrier();
-  asm volatile("" ::: "memory");
-  if (!wave_on) return;
-  uint8_t *ep = smem + wave * (KIND == kGateUp ? kBlockM * 64 : kBlockM * 128);
-  store_block<KIND>(acc, st.nrb, KIND == kGateUp ? n0 + wave * 32 : n0 + wave * 64, shared,
-                    row_begin, row_end, TK, d, f, ep, out_bf16, out_f32);
 }
+
+// Batches of up to 32 tokens take the MRB = 1 kernel. With distinct experts
+// per token (the library's own routing) no group has more rows than tokens,
+// so every tile is one pass; caller ids that repeat an expert make taller
+// groups, which take several passes. (Up to 64 tokens it was no faster: the
+// shared expert's two-block tile, run as two passes, became the launch's
+// longest work item.)
+constexpr int kShortTileMaxT = 32;
 
 static long long round_up8(long long n) { return (n + kXcds - 1) / kXcds * kXcds; }
 
 // LDS of one GEMM workgroup for input width K: the activation ring and the
-// scale/bias table (K/64 groups x 256 weight rows x 4 bytes).
+// scale/bias table (K/64 groups x 256 weight rows x 4 bytes), and the output
+// staging (per wavefront its rows x 128 bytes for down, x 64 for gate/up):
+// over the ring and table in the full-tile kernel, after the table in the
+// MRB = 1 down kernel.
+template <int KIND, int MRB>
 static size_t gemm_lds_bytes(int K) {
-  const size_t loop = (size_t)kStages * kStageBytes + (size_t)(K / kGroup) * kWgCols * 4;
-  const size_t epilogue = (size_t)kWaves * kBlockM * 128;  // per wavefront kBlockM rows x 128 bytes (down)
+  const size_t loop = (size_t)kStages * stage_bytes<MRB>() + (size_t)(K / kGroup) * kWgCols * 4;
+  const size_t epilogue = (size_t)kWaves * MRB * 32 * (KIND == kGateUp ? 64 : 128);
+  if (MRB == 1 && KIND == kDown) return loop + epilogue;
   return loop > epilogue ? loop : epilogue;
 }
 
 // More than 64 KB of dynamic LDS needs a per-kernel opt-in (once per process).
 static hipError_t gemm_setup() {
   static const hipError_t st = [] {
-    const int max_lds = (int)gemm_lds_bytes(kGemmMaxK);
-    hipError_t e = hipFuncSetAttribute((const void *)grouped_gemm_w4_kernel<kGateUp>,
-                                       hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
-    if (e == hipSuccess)
-      e = hipFuncSetAttribute((const void *)grouped_gemm_w4_kernel<kDown>,
-                              hipFuncAttributeMaxDynamicSharedMemorySize, max_lds);
+    const void *kernels[4] = {(const void *)grouped_gemm_w4_kernel<kGateUp, kRB>,
+                              (const void *)grouped_gemm_w4_kernel<kDown, kRB>,
+                              (const void *)grouped_gemm_w4_kernel<kGateUp, 1>,
+                              (const void *)grouped_gemm_w4_kernel<kDown, 1>};
+    const int max_lds[4] = {(int)gemm_lds_bytes<kGateUp, kRB>(kGemmMaxK),
+                            (int)gemm_lds_bytes<kDown, kRB>(kGemmMaxK),
+                            (int)gemm_lds_bytes<kGateUp, 1>(kGemmMaxK),
+                            (int)gemm_lds_bytes<kDown, 1>(kGemmMaxK)};
+    hipError_t e = hipSuccess;
+    for (int i = 0; i < 4 && e == hipSuccess; ++i)
+      e = hipFuncSetAttribute(kernels[i], hipFuncAttributeMaxDynamicSharedMemorySize, max_lds[i]);
     return e;
   }();
   return st;
@@ -583,9 +654,14 @@ hipError_t launch_gate_up(const Dims &dm, const uint16_t *x, const Weights &w,
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.f + kWgCols / 2 - 1) / (kWgCols / 2);
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
-  grouped_gemm_w4_kernel<kGateUp><<<grid, kThreads, gemm_lds_bytes(dm.d), s>>>(
-      x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
-      dm.k);
+  if (dm.T <= kShortTileMaxT)
+    grouped_gemm_w4_kernel<kGateUp, 1><<<grid, kThreads, gemm_lds_bytes<kGateUp, 1>(dm.d), s>>>(
+        x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
+        dm.k);
+  else
+    grouped_gemm_w4_kernel<kGateUp, kRB><<<grid, kThreads, gemm_lds_bytes<kGateUp, kRB>(dm.d), s>>>(
+        x, w.w13, w.s13, sorted_token, tile_map, num_tiles, h, nullptr, dm.T, dm.d, dm.f, dm.E,
+        dm.k);
   return hipGetLastError();
 }
 
@@ -596,9 +672,14 @@ hipError_t launch_down(const Dims &dm, const uint16_t *h, const Weights &w,
   if (const hipError_t e = gemm_setup()) return e;
   const int nblk = (dm.d + kWgCols - 1) / kWgCols;
   const int grid = (int)(nblk * round_up8(tile_capacity(dm)));
-  grouped_gemm_w4_kernel<kDown><<<grid, kThreads, gemm_lds_bytes(dm.f), s>>>(
-      h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
-      dm.k);
+  if (dm.T <= kShortTileMaxT)
+    grouped_gemm_w4_kernel<kDown, 1><<<grid, kThreads, gemm_lds_bytes<kDown, 1>(dm.f), s>>>(
+        h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
+        dm.k);
+  else
+    grouped_gemm_w4_kernel<kDown, kRB><<<grid, kThreads, gemm_lds_bytes<kDown, kRB>(dm.f), s>>>(
+        h, w.w2, w.s2, nullptr, tile_map, num_tiles, o_routed, o_shared, dm.T, dm.d, dm.f, dm.E,
+        dm.k);
   return hipGetLastError();
 }
 

@@ -340,3 +340,59 @@ def test_zero_tokens_is_noop():
     M.moe_layer_forward(dm, x, logits, w, y=y, ws=torch.empty(256, dtype=torch.uint8, device="cuda"))
     torch.cuda.synchronize()
     assert (y == 7.0).all()
+
+
+# A block map whose groups have more rows than there are tokens, as ids that
+# repeat an expert within a token would give. moe_permute requires distinct
+# ids per token, so the map is built here from the oracle's steps and handed
+# to the grouped GEMMs directly. Up to 32 tokens the GEMMs run the kernel
+# compiled for one-row-block tiles, which takes a taller tile in 32-row
+# passes. The largest group here: 61 rows (one tile, two passes), 256 rows
+# (two full tiles, four passes each) and 108 rows (four passes).
+REPEAT_IDS = [
+    G.small_config("rep_t24_k4_e4", T=24, d=128, f=64, E=4, k=4, seed=96),
+    G.small_config("rep_t32_k8_e8_all0", T=32, d=192, f=128, E=8, k=8, seed=97),
+    G.small_config("rep_t17_k8_e8", T=17, d=2048, f=512, E=8, k=8, seed=98, bias_mode=G.BIAS_MIXED),
+]
+
+
+def _repeat_ids(cfg):
+    r = np.random.default_rng(cfg.seed)
+    T, k, E = cfg.T, cfg.k, cfg.E
+    if cfg.name.endswith("all0"):
+        return np.zeros((T, k), dtype=np.int32)
+    ids = r.integers(0, E, size=(T, k)).astype(np.int32)
+    ids[r.random((T, k)) < 0.7] = 0
+    return ids
+
+
+@pytest.mark.parametrize("cfg", REPEAT_IDS, ids=lambda c: c.name)
+def test_tall_groups_from_repeated_ids(cfg):
+    say(f"[tall groups] {cfg.name}")
+    T, k, E = cfg.T, cfg.k, cfg.E
+    inp = inputs(cfg)
+    ids = _repeat_ids(cfg)
+    r = np.random.default_rng(cfg.seed + 1)
+    wts = r.random((T, k)).astype(np.float32)
+    wts /= wts.sum(axis=1, keepdims=True)
+    counts = O.histogram(ids, E)
+    offsets = O.exclusive_scan(counts)
+    sorted_token, row_of = O.scatter(ids, offsets)
+    tiles = O.block_map(counts, offsets, T, k, M.moe_block_m())
+    assert counts.max() > 32  # some tile needs more than one pass
+    h_ref, o_ref = O.expert_ffn(O.bf16_to_f64(inp["x"]), sorted_token, counts, offsets,
+                                inp["weights"], T, k)
+    y_ref = O.combine(o_ref, wts.astype(np.float64), row_of, T, k)
+
+    dm, x, _, w = upload(inp)
+    tmap = np.zeros((M.moe_tile_capacity(dm), 4), dtype=np.int32)
+    tmap[:len(tiles), :3] = tiles
+    tmap[:len(tiles), 3] = expected_schedule(tiles)
+    dev_i32 = lambda a: torch.from_numpy(np.ascontiguousarray(a, dtype=np.int32)).cuda()
+    h, o_r, o_sh = M.moe_expert_ffn_w4(dm, x, w, dev_i32(sorted_token), dev_i32(tmap),
+                                       dev_i32([len(tiles), 0, 0, 0]))
+    y = M.moe_unpermute_combine(dm, o_r, o_sh, torch.from_numpy(wts).cuda(), dev_i32(row_of))
+    torch.cuda.synchronize()
+    ref = dict(offsets=offsets, sorted_token=sorted_token)
+    check_bf16_close(host_bits(h), h_ref, "h", max_frac=0.02, slack=_h_slack(cfg, inp, ref))
+    check_y(y.cpu().numpy(), y_ref)
