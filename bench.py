@@ -19,7 +19,8 @@ step, inputs resident in HBM. Also reported on the same JSON line:
   cpu_baseline  the CPU oracle on the whole headline layer (and, under
                 configs, on the whole layer of each other workload);
   small_batch   the layer at T = 1, 2, 8, 32, 64 (skipped with
-                --no-small-batch), bytes of the used experts' weights / time.
+                --no-small-batch), bytes of the used experts' weights / time,
+                timed in 32-call HIP graphs (us) and call by call (us_eager).
 Usage: python bench.py [--steps K] [--warmup W] [--gpus 1]
 """
 import argparse
@@ -345,7 +346,9 @@ def main():
 
     # ---------------------------------------------------------------- small batches
     # moe_layer_forward at T = 1 .. 64 (the general path; T = 1 takes the
-    # decode kernels), two weight copies alternated, events around 100 calls
+    # decode kernels), two weight copies alternated: a HIP graph of 32 calls
+    # replayed three times (as a serving loop would run them), and events
+    # around 100 calls issued one by one
     small = None
     if not args.no_small_batch:
         log("[bench] small batches")
@@ -369,10 +372,25 @@ def main():
                 M.moe_layer_forward(dms, xs, ls, w, y=ys, ws=wss, wc=wcs[i % 2])
             e1.record()
             torch.cuda.synchronize()
-            us = e0.elapsed_time(e1) * 10.0
+            us_eager = e0.elapsed_time(e1) * 10.0
+            graph, gs = torch.cuda.CUDAGraph(), torch.cuda.Stream()
+            with torch.cuda.stream(gs):
+                with torch.cuda.graph(graph, stream=gs):
+                    for i in range(32):
+                        M.moe_layer_forward(dms, xs, ls, w, y=ys, ws=wss, wc=wcs[i % 2])
+            torch.cuda.synchronize()
+            graph.replay()
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(3):
+                graph.replay()
+            e1.record()
+            torch.cuda.synchronize()
+            us = e0.elapsed_time(e1) * 1e3 / 96
+            del graph
             by = (ne + 1) * expert_bytes(d, f) + Ts * (d * 2 + E * 4 + d * 4)
-            small[f"T={Ts}"] = {"us": round(us, 2), "experts": ne, "bytes": by,
-                                "GB/s": round(by / us / 1e3, 1),
+            small[f"T={Ts}"] = {"us": round(us, 2), "us_eager": round(us_eager, 2), "experts": ne,
+                                "bytes": by, "GB/s": round(by / us / 1e3, 1),
                                 "frac_hbm": round(by / us / 1e3 / PEAK_HBM_GBPS, 4)}
         del w2
         log(f"[bench] small batches: {small}")
