@@ -188,9 +188,12 @@ moe_status moe_route_permute(const moe_dims *dm, const float *logits, int32_t *t
 
 /*
  * moe_expert_gate_up_w4 - grouped gate/up GEMM over the block map with the
- * int4-g64 dequantisation fused into the tile (bf16 MFMA operands rebuilt in
- * LDS one K-tile at a time, fp32 accumulation; page section "Prefill e
- * decode: onde estao os ganhos"), and SiLU(gate)*up in the epilogue.
+ * int4-g64 dequantisation fused into the tile (the weights' bf16 MFMA
+ * operands rebuilt in registers one K step at a time, fp32 accumulation; page
+ * section "Prefill e decode: onde estao os ganhos"), and SiLU(gate)*up in the
+ * epilogue. The block map may also be built by the caller: tiles of at most
+ * moe_block_m() rows of one group, in moe_permute's layout, with a schedule
+ * column that is a permutation of the tile indices.
  *   x            bf16  [T][d]
  *   sorted_token int32 [T*k], tile_map, num_tiles from moe_permute
  *   h            bf16  [T*k+T][f] out: h[p] = bf16(silu(gate_p) * up_p), with
