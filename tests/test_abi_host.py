@@ -94,6 +94,10 @@ def test_dims_validation(L):
     assert f(ctypes.byref(_dims(f_shared=0))) == 0
     assert f(ctypes.byref(_dims())) > 0
     assert L.moe_tile_capacity(ctypes.byref(_dims(d=100))) == -1
+    # the largest batch: T * (k + 1) rows of max(d, 2f) elements under 2^31
+    # (116,508 tokens at the headline widths)
+    assert f(ctypes.byref(_dims(T=116508, d=2048, f=512, E=256, k=8))) > 0
+    assert f(ctypes.byref(_dims(T=116509, d=2048, f=512, E=256, k=8))) == 0
     # workspace grows with T
     a = f(ctypes.byref(_dims(T=100, d=2048, f=512, E=256, k=8)))
     b = f(ctypes.byref(_dims(T=200, d=2048, f=512, E=256, k=8)))

@@ -96,6 +96,40 @@ def test_full_size_prefill(name):
     check_y(yh[toks], ref, f"y[{len(toks)} sampled tokens]")
 
 
+# Many tokens at narrow widths: a million tokens over 4,097 permutation
+# blocks (each placement workgroup scans every earlier block's counts), and
+# 262,144 Zipf-routed tokens over 256 experts (1,025 blocks); routing,
+# permutation and block map in full, y on sampled tokens.
+MANY = [
+    G.small_config("many_t1m_e8_k2", T=1 << 20, d=128, f=64, E=8, k=2, seed=101),
+    G.small_config("many_t262k_e256_k8", T=1 << 18, d=64, f=64, E=256, k=8, seed=102,
+                   zipf_s=1.1),
+]
+
+
+@pytest.mark.parametrize("cfg", MANY, ids=lambda c: c.name)
+def test_many_tokens(cfg):
+    say(f"[many tokens] {cfg.name}: routing + permutation")
+    inp = G.make_layer_inputs(cfg)
+    dm, x, logits, w = upload(inp)
+    counts = _check_routing(cfg, inp, dm, logits)
+    say(f"[many tokens] {cfg.name}: layer forward")
+    y = M.moe_layer_forward(dm, x, logits, w)
+    torch.cuda.synchronize()
+    yh = y.cpu().numpy()
+    assert np.isfinite(yh).all()
+    r = np.random.default_rng(cfg.seed)
+    rid, _ = O.route(inp["logits"], cfg.k)
+    offsets = O.exclusive_scan(counts)
+    st, _ = O.scatter(rid, offsets)
+    picks = [r.choice(cfg.T, 24, replace=False), [0, cfg.T - 1]]
+    for g in np.nonzero(counts)[0]:
+        picks.append([st[int(offsets[g])], st[int(offsets[g + 1]) - 1]])
+    toks = np.unique(np.concatenate([np.asarray(p, dtype=np.int64) for p in picks]))
+    ref = O.token_outputs(inp["x"], inp["logits"], inp["weights"], cfg.k, toks)
+    check_y(yh[toks], ref, f"y[{len(toks)} sampled tokens]")
+
+
 def test_decode_b1():
     cfg = G.CONFIGS["decode_b1"]
     say("[decode] routing of all 1000 steps")
