@@ -26,6 +26,10 @@ GROUPED = [
                    bias_mode=GENERAL),
     G.small_config("gb_full_width_t300_mixed", T=300, d=2048, f=512, E=256, k=8, seed=85,
                    bias_mode=MIXED),
+    # up to 32 tokens: the grouped GEMMs' one-row-block build, with wavefronts
+    # of both K loops in one launch
+    G.small_config("gb_full_width_t24_mixed", T=24, d=2048, f=512, E=256, k=8, seed=114,
+                   bias_mode=MIXED),
 ]
 # the layer's per-token decode kernels (T <= 16) and, through the staged entry
 # points, the VALU projections (T <= 6) or one-row-block grouped GEMM tiles
