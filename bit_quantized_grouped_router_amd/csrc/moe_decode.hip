@@ -85,6 +85,12 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   const int item = gw * U;
   const int slot = item / f, n = item % f;
   const bool shared = slot == k;
+  // the top-k runs once per workgroup (wavefront 0; the other three wait at
+  // the barrier instead of repeating it); its logits are loaded first, so
+  // that their round trip overlaps the staging of x below instead of
+  // following it
+  float lv[kMaxPerLane];
+  if (wave == 0 && !shared) wave_load_logits<kMaxPerLane>(logits, E, lv);
   // x's first kDecXCols columns, staged in LDS once per workgroup before the
   // routing (independent of it): each wavefront loads a quarter, 16 bytes per
   // lane, instead of every wavefront loading all of them from the caches
@@ -92,16 +98,14 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
     const int c = (wave * kWave + lane) * 8;
     if (c < d && c < kDecXCols) *(uint4 *)(s_x + c) = *(const uint4 *)(x + c);
   }
-  // the top-k once per workgroup (wavefront 0; the other three wait at the
-  // barrier instead of repeating it), shared through LDS
-  // A workgroup of slot j needs only the first j + 1 selection rounds; the
-  // first workgroup of the last routed slot takes all k and writes the
-  // token's ids and weights.
+  // the selection, shared through LDS. A workgroup of slot j needs only the
+  // first j + 1 selection rounds; the first workgroup of the last routed slot
+  // takes all k and writes the token's ids and weights.
   if (wave == 0 && !shared) {
     int id;
     float l;
     const bool writer = slot == k - 1 && n == 0;
-    wave_topk<kMaxPerLane>(logits, E, writer ? k : slot + 1, &id, &l);
+    wave_topk_loaded<kMaxPerLane>(lv, E, writer ? k : slot + 1, &id, &l);
     if (lane == slot) s_expert = id;
     if (writer) {
       const float m = __shfl(l, 0, kWave);
