@@ -202,10 +202,14 @@ __global__ __launch_bounds__(1024) void decode_down_slots_kernel(
   float acc = 0.f;
   for (int j = wave; j <= k; j += W) {
     const bool sh = j == k;
-    const int e = sh ? 0 : min(max(ids[j], 0), E - 1);  // in range for any ids
-    const float wj = sh ? 1.f : wts[j];
+    // the slot's h columns do not depend on the id: their loads go out first
+    // and stay in flight while the id's scalar load returns (the scheduling
+    // barrier keeps the compiler from sinking them below its wait)
     const uint4 *hp = (const uint4 *)(h + (size_t)j * f + c0);
     const uint4 hv[4] = {hp[0], hp[1], hp[2], hp[3]};
+    __builtin_amdgcn_sched_barrier(0);
+    const int e = sh ? 0 : min(max(ids[j], 0), E - 1);  // in range for any ids
+    const float wj = sh ? 1.f : wts[j];
     const W4 M = sh ? s2 : w2;
     const size_t row = (size_t)e * d + m;
     const uint4 cv = *(const uint4 *)(M.codes + row * (size_t)(f / 2) + c0 / 2);
