@@ -100,24 +100,30 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   }
   // the selection, shared through LDS. A workgroup of slot j needs only the
   // first j + 1 selection rounds; the first workgroup of the last routed slot
-  // takes all k and writes the token's ids and weights.
+  // takes all k and writes the token's ids and weights, at its end, so that
+  // no store is outstanding at the barrier below.
+  const bool writer = wave == 0 && !shared && slot == k - 1 && n == 0;  // wave-uniform
+  int wid = 0;
+  float ww = 0.f;
   if (wave == 0 && !shared) {
     int id;
     float l;
-    const bool writer = slot == k - 1 && n == 0;
     wave_topk_loaded<kMaxPerLane>(lv, E, writer ? k : slot + 1, &id, &l);
     if (lane == slot) s_expert = id;
     if (writer) {
       const float m = __shfl(l, 0, kWave);
       const float e = lane < k ? expf(l - m) : 0.f;
       const float sum = wave_sum(e);
-      if (lane < k) {
-        ids_out[lane] = id;
-        wts_out[lane] = e / sum;
-      }
+      wid = id;
+      ww = e / sum;
     }
   }
-  __syncthreads();
+  // x and the chosen expert are in LDS; the barrier waits for LDS operations
+  // only, not for the global loads the other wavefronts may have in flight
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_waitcnt(0xF | (0x7 << 4) | (0x0 << 8) | (0x3 << 14));  // lgkmcnt(0)
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
   // this lane's first 32 columns of x (lane * 32 < kDecXCols always)
   uint4 xv0[4] = {};
   if (lane * 32 < d) {
@@ -166,6 +172,10 @@ __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
   if (lane == 0) {
 #pragma unroll
     for (int u = 0; u < U; ++u) h[(size_t)slot * f + n + u] = to_bf16(silu_mul(acc[u], acc[U + u]));
+  }
+  if (writer && lane < k) {
+    ids_out[lane] = wid;
+    wts_out[lane] = ww;
   }
 }
 
