@@ -57,10 +57,10 @@ __device__ __forceinline__ float dot32_any(uint4 c, uint32_t sb, const uint4 *xv
 }
 
 // One wavefront = one slot (routed slot j < k, or the shared expert at
-// j == k) and U intermediate units (a gate row and an up row each). Loads
-// are issued as early as their addresses are known: x first, the shared
-// expert's rows at once, a routed slot's rows right after the workgroup's
-// on-chip top-k.
+// j == k) and U intermediate units (a gate row and an up row each). The
+// logits and x are loaded first, together; past the workgroup's barrier each
+// wavefront loads its slot's weight rows (a routed slot's once the on-chip
+// top-k has chosen the expert).
 template <int kMaxPerLane, int U>
 __global__ __launch_bounds__(kDecWaves * 64) void decode_gate_up_kernel(
     const uint16_t *__restrict__ x, const float *__restrict__ logits, W4 w13, W4 s13, int d,
