@@ -101,9 +101,11 @@ typedef struct {
  * (page section "O modelo em tres formatos de carga": the router scores the
  * E experts), as a bias-free projection of the hidden states:
  *   logits[t][e] = sum_c x[t][c] * w_router[e][c]
- * Products of two bf16 values are exact in fp32; they are summed in fp32 on
- * the matrix cores (the summation order is unspecified, so results may differ
- * from another fp32 order by rounding, within d * 2^-24 * sum_c |x w|).
+ * Products of two bf16 values are exact in fp32; they are summed in fp32, on
+ * the matrix cores above 128 tokens and as dot products on the vector units
+ * up to 128 (the summation order is unspecified but fixed, so results may
+ * differ from another fp32 order by rounding, within d * 2^-24 * sum_c |x w|,
+ * and repeat bit for bit).
  *   x         bf16 [T][d]   hidden states
  *   w_router  bf16 [E][d]   router matrix
  *   logits    fp32 [T][E]   out

@@ -33,6 +33,23 @@ CASES = [
     # multiple of 64): 129 K steps, an odd count split over the two K halves
     G.small_config("rt_t33_d8256_e24", T=33, d=8256, f=64, E=24, k=4, seed=60),
     G.small_config("rt_t4096_d2048_e256", T=4096, d=2048, f=512, E=256, k=8, seed=57),
+    # Up to 128 tokens the scores are dot products on the VALU (one wavefront
+    # per expert and block of 4 tokens, 2048 columns per pass), so every case
+    # above with T <= 128 runs there; these also do: a ragged token block, a
+    # partial pass and an expert count that leaves workgroups partly empty;
+    # three whole passes; five passes, the last partial; the largest batch.
+    G.small_config("rt_t5_d192_e37", T=5, d=192, f=64, E=37, k=5, seed=115),
+    G.small_config("rt_t16_d6144_e64", T=16, d=6144, f=64, E=64, k=8, seed=116),
+    G.small_config("rt_t3_d8256_e24", T=3, d=8256, f=64, E=24, k=4, seed=117),
+    G.small_config("rt_t128_d2048_e256", T=128, d=2048, f=512, E=256, k=8, seed=118),
+    # and the MFMA tiles on the shapes above that stress them: a ragged K
+    # round (10 K steps), expert counts that are not a multiple of 4 (row
+    # tails), an odd number of K steps over the two halves, the widest input
+    G.small_config("rt_t137_d192_e8", T=137, d=192, f=64, E=8, k=2, seed=119),
+    G.small_config("rt_t192_d640_e64", T=192, d=640, f=64, E=64, k=8, seed=120),
+    G.small_config("rt_t170_d320_e37", T=170, d=320, f=64, E=37, k=5, seed=121),
+    G.small_config("rt_t133_d8256_e24", T=133, d=8256, f=64, E=24, k=4, seed=122),
+    G.small_config("rt_t165_d6144_e100", T=165, d=6144, f=64, E=100, k=4, seed=123),
 ]
 
 
@@ -83,10 +100,12 @@ def test_router_scores_and_routing(cfg):
     assert torch.equal(again, logits)
 
 
-def test_router_unit_rows_copy_columns():
+@pytest.mark.parametrize("T", [170, 7])
+def test_router_unit_rows_copy_columns(T):
     # Wr rows with a single 1.0: each score is one hidden-state value, exactly
-    T, d, E = 70, 256, 72
-    r = np.random.default_rng(58)
+    # (170 tokens: the MFMA tiles; 7: the dot products)
+    d, E = 256, 72
+    r = np.random.default_rng(58 if T == 170 else 65)
     x = G.f32_to_bf16_bits(r.standard_normal((T, d)).astype(np.float32))
     cols = r.integers(0, d, size=E)
     w = np.zeros((E, d), np.float32)
