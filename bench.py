@@ -10,7 +10,8 @@ step, inputs resident in HBM. Also reported on the same JSON line:
   kernels       every kernel's mean duration and rate;
   decode        batch-1 decode: 1000 steps through the T=1 path, 32 weight
                 copies rotated so no step re-reads weights from cache, replayed
-                as a HIP graph; algorithmic bytes / time per step;
+                as a HIP graph; algorithmic bytes / time per step; and the
+                first 256 steps from hidden states (router projection first);
   configs       the other workloads: T=16 (median latency), T=512 (two
                 weight copies alternated; GB/s of the used experts' weights and
                 I/O against 8 TB/s), T=16384 with 8 forced-empty experts
@@ -453,6 +454,39 @@ def main():
             us_graph = e0.elapsed_time(e1) * 1e3 / args.decode_steps
         except Exception as ex:  # graph capture unavailable: keep the stream figure
             log(f"[bench] decode graph capture failed: {ex}")
+        # the first 256 steps again from hidden states: the router projection
+        # (x . Wr^T) and the layer, in graphs of n_copies steps
+        us_hidden = None
+        try:
+            wrd = torch.from_numpy(G.make_router(dcfg).view(np.int16)).to(dev)
+            nh = min(256, args.decode_steps)
+
+            def run_hidden(lo, hi, st=None):
+                for s in range(lo, hi):
+                    M.moe_layer_forward_hidden(dmd, xs[s:s + 1], wrd, None, y=yd[s:s + 1], ws=wsd,
+                                               wc=cstructs[s % n_copies], stream=st)
+
+            run_hidden(0, min(n_copies, nh))
+            torch.cuda.synchronize()
+            hgraphs, hs = [], torch.cuda.Stream()
+            with torch.cuda.stream(hs):
+                for lo in range(0, nh, n_copies):
+                    g = torch.cuda.CUDAGraph()
+                    with torch.cuda.graph(g, stream=hs):
+                        run_hidden(lo, min(lo + n_copies, nh), st=hs)
+                    hgraphs.append(g)
+            torch.cuda.synchronize()
+            hgraphs[0].replay()
+            torch.cuda.synchronize()
+            e0.record(stream)
+            for g in hgraphs:
+                g.replay()
+            e1.record(stream)
+            torch.cuda.synchronize()
+            us_hidden = e0.elapsed_time(e1) * 1e3 / nh
+            del hgraphs
+        except Exception as ex:  # graph capture unavailable
+            log(f"[bench] decode from hidden states: graph capture failed: {ex}")
         bytes_step = 9 * expert_bytes(dcfg.d, dcfg.f) + dcfg.d * 2 + dcfg.E * 4 + dcfg.d * 4
         best = us_graph if us_graph is not None else us_stream
         decode = {"workload": "decode_b1 (T=1, d=2048, f=512, E=256, top-8 + shared, 1000 steps)",
@@ -461,6 +495,7 @@ def main():
                   "frac_hbm": round(bytes_step / (best * 1e-6) / 1e9 / PEAK_HBM_GBPS, 4),
                   "us_per_step_stream_loop": round(us_stream, 3),
                   "us_per_step_graph": None if us_graph is None else round(us_graph, 3),
+                  "us_per_step_from_hidden_states": None if us_hidden is None else round(us_hidden, 3),
                   "tok/s": round(1e6 / best, 1), "weight_copies": n_copies}
         log(f"[bench] decode: {decode}")
         del copies, cstructs
