@@ -119,6 +119,10 @@ LAYER_CASES = [
     G.small_config("hid_t300", T=300, d=256, f=128, E=16, k=4, seed=61),
     G.small_config("hid_t1_decode", T=1, d=2048, f=512, E=64, k=8, seed=62),
     G.small_config("hid_t2", T=2, d=128, f=64, E=8, k=8, seed=63),
+    # the router's dot products ahead of the grouped path: the one-row-block
+    # GEMM build (24 tokens) and the full-tile build (100 tokens)
+    G.small_config("hid_t24", T=24, d=512, f=256, E=32, k=8, seed=124),
+    G.small_config("hid_t100", T=100, d=256, f=128, E=16, k=4, seed=125),
 ]
 
 
