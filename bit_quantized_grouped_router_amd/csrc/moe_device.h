@@ -286,13 +286,10 @@ __device__ __forceinline__ void wave_topk_sorted(const float (&v)[kMaxPerLane], 
   static_assert(kMaxPerLane >= 1 && kMaxPerLane <= 4, "sorted selection: up to 4 keys per lane");
   constexpr int M = kMaxPerLane;
   const int lane = threadIdx.x & (kWave - 1);
-  uint32_t key[M];
-  int slot[M];
+  uint32_t key[4] = {0u, 0u, 0u, 0u};  // entries past M stay 0 (empty)
+  int slot[4] = {0, 1, 2, 3};
 #pragma unroll
-  for (int i = 0; i < M; ++i) {
-    key[i] = lane + i * kWave < E ? logit_key(v[i]) : 0u;
-    slot[i] = i;
-  }
+  for (int i = 0; i < M; ++i) key[i] = lane + i * kWave < E ? logit_key(v[i]) : 0u;
 #pragma unroll
   for (int pass = 0; pass < M; ++pass)
 #pragma unroll
@@ -305,33 +302,36 @@ __device__ __forceinline__ void wave_topk_sorted(const float (&v)[kMaxPerLane], 
         slot[i] = slot[i + 1];
         slot[i + 1] = ts;
       }
+  // the list's slots, one byte each (byte i: slot of key[i]), so that the
+  // winning lane's shift below is one register shift
+  uint32_t slots = 0;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) slots |= (uint32_t)slot[i] << (8 * i);
+  // the list as four named registers inside the loop
+  uint32_t k0 = key[0], k1 = key[1], k2 = key[2], k3 = key[3];
   int my_id = 0;
   float my_logit = 0.f;
   for (int j = 0; j < k; ++j) {
-    const uint32_t m = wave_max_u32(key[0]);
-    const uint64_t tied = __builtin_amdgcn_ballot_w64(key[0] == m);
-    int wl;
-    if (__builtin_popcountll(tied) == 1) {
-      wl = __builtin_ctzll(tied);
-    } else {
+    const uint32_t m = wave_max_u32(k0);
+    const uint64_t tied = __builtin_amdgcn_ballot_w64(k0 == m);
+    int wl = __builtin_ctzll(tied);
+    if (__builtin_expect((tied & (tied - 1)) != 0, 0)) {
       // lowest expert index lane + 64 * slot among the lanes holding key m first
-      const uint32_t idx = (uint32_t)(lane + kWave * slot[0]);
-      wl = (int)(~wave_max_u32(key[0] == m ? ~idx : 0u) & (kWave - 1));
+      const uint32_t idx = (uint32_t)(lane + kWave * (int)(slots & 0xffu));
+      wl = (int)(~wave_max_u32(k0 == m ? ~idx : 0u) & (kWave - 1));
     }
-    int id = wl + kWave * __builtin_amdgcn_readlane(slot[0], wl);
+    int id = wl + kWave * (int)(__builtin_amdgcn_readlane(slots, wl) & 0xffu);
     if (id >= E) id = 0;  // unreachable while k <= E; keeps ids in range
-    if (lane == wl) {
-#pragma unroll
-      for (int i = 0; i + 1 < M; ++i) {
-        key[i] = key[i + 1];
-        slot[i] = slot[i + 1];
-      }
-      key[M - 1] = 0u;
-    }
-    if (lane == j) {
-      my_id = id;
-      my_logit = key_logit(m);
-    }
+    // the winning lane drops its first key (selects, no branch)
+    const bool win = lane == wl;
+    k0 = win ? k1 : k0;
+    k1 = win ? k2 : k1;
+    k2 = win ? k3 : k2;
+    k3 = win ? 0u : k3;
+    slots = win ? slots >> 8 : slots;
+    const bool mine = lane == j;
+    my_id = mine ? id : my_id;
+    my_logit = mine ? key_logit(m) : my_logit;
   }
   *out_id = my_id;
   *out_logit = my_logit;
