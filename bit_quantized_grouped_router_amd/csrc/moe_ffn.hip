@@ -46,7 +46,6 @@ constexpr int kRB = kBlockM / 32;            // 32-row blocks per tile
 constexpr int kStages = 3;                   // activation ring depth
 constexpr int kDmaRows = kThreads / 8;        // tile rows one DMA instruction of the workgroup fills
 static_assert(kWaves % 2 == 0 && kBlockM % kDmaRows == 0 && kDmaRows == 32, "DMA row mapping");
-constexpr int kXcds = 8;
 
 // The kernel is compiled twice: for tiles of up to MRB = kRB row blocks (the
 // block map's full tiles), and for MRB = 1, used when no tile of the launch

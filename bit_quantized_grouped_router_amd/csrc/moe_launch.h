@@ -12,6 +12,9 @@ namespace moe {
 
 // Rows per tile of the block map, shared by both grouped GEMMs.
 constexpr int kBlockM = 128;
+// XCDs of the chip: the grouped GEMMs deal schedule position i to XCD i % 8
+// (workgroups go to the XCDs round-robin), and the schedule is built for it.
+constexpr int kXcds = 8;
 // Largest input width of a grouped GEMM: a tile keeps the scales and biases
 // of its 256 weight rows for all K/64 groups in LDS, next to 64 KB of
 // activation buffers (1 KB per group, 160 KB of LDS per CU).

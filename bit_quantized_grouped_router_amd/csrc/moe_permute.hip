@@ -84,10 +84,24 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *wave_tot) {
 
 // Tiles are full (kBlockM rows) except the last of each group (c % kBlockM
 // rows). The schedule (fourth column of the tile map: row i names the i-th
-// tile to run) lists every full tile in tile order, then the partial tiles
-// by decreasing height, equal heights in tile order. Partial tiles are
-// ranked with one LDS bitmask of groups per height, so the order is exact
-// and independent of the order atomics happen in.
+// tile to run) lists every full tile first, then the partial tiles by
+// decreasing height, equal heights in tile order. Partial tiles are ranked
+// with one LDS bitmask of groups per height, so the order is exact and
+// independent of the order atomics happen in.
+// The grouped GEMMs deal schedule position i to XCD i % kXcds. The full
+// tiles, in tile order, are cut into kXcds runs of equal length (the first
+// nfull % kXcds one tile longer), and run x goes to positions x, x + kXcds,
+// x + 2 kXcds, ...: each XCD gets consecutive tiles, so a hot expert's full
+// tiles share one XCD's L2 instead of every XCD fetching that expert's
+// weights. Each XCD still receives the same positions, hence the same number
+// of tiles of each height. Position of full tile p (0 <= p < nfull):
+__device__ __forceinline__ int full_tile_position(int p, int nfull) {
+  const int q = nfull / kXcds, rem = nfull % kXcds;
+  const int big = rem * (q + 1);  // tiles in the longer runs
+  if (p < big) return kXcds * (p % (q + 1)) + p / (q + 1);
+  const int p2 = p - big;  // here q >= 1, since p < nfull
+  return kXcds * (p2 % q) + rem + p2 / q;
+}
 constexpr int kMaxGroups = kMaxExperts + 1;
 constexpr int kGroupWords = (kMaxGroups + 31) / 32;
 
@@ -167,7 +181,8 @@ __device__ void write_tile_map(PlaceLds &L, int c, int c_incl, int T, int E, int
   __syncthreads();
   // schedule entries: full routed tiles, full shared tiles, partial tiles
   if (e < E) {
-    for (int i = 0; i < nf; ++i) tile_map[4 * (size_t)(fbase + i) + 3] = tbase + i;
+    for (int i = 0; i < nf; ++i)
+      tile_map[4 * (size_t)full_tile_position(fbase + i, nfull) + 3] = tbase + i;
     const int r = c % kBlockM;
     if (r) {
       int rank = __popc(L.u.m.hmask[r][e >> 5] & ((1u << (e & 31)) - 1u));
@@ -176,7 +191,7 @@ __device__ void write_tile_map(PlaceLds &L, int c, int c_incl, int T, int E, int
     }
   }
   for (int i = e; i < T / kBlockM; i += kPlaceThreads)
-    tile_map[4 * (size_t)(L.routed_full + i) + 3] = rbase + i;
+    tile_map[4 * (size_t)full_tile_position(L.routed_full + i, nfull) + 3] = rbase + i;
   if (e == 0 && T % kBlockM) {
     const int r = T % kBlockM;
     int rank = 0;

@@ -155,10 +155,16 @@ size_t moe_permute_workspace_bytes(const moe_dims *dm);
  *                                     split into ceil(count/BM) tiles of at most
  *                                     BM = moe_block_m() rows. sched of row i is
  *                                     the index of the i-th tile in the order
- *                                     the grouped GEMMs run them: tallest tile
- *                                     first, equal heights in tile order (a
- *                                     permutation of 0..num_tiles-1). Entries
- *                                     past num_tiles are left untouched.
+ *                                     the grouped GEMMs run them (position i
+ *                                     on XCD i % 8), a permutation of
+ *                                     0..num_tiles-1: first the F full tiles,
+ *                                     in tile order cut into 8 runs whose
+ *                                     lengths differ by at most one (longer
+ *                                     runs first), the r-th tile of run x at
+ *                                     position 8r + x; then the partial tiles,
+ *                                     tallest first, equal heights in tile
+ *                                     order. Entries past num_tiles are left
+ *                                     untouched.
  *   num_tiles    int32 [1]            out: tiles written
  *   ws, ws_bytes                      scratch, >= moe_permute_workspace_bytes(dm)
  * Deterministic: the row order does not depend on scheduling.

@@ -69,12 +69,28 @@ def check_bf16_close(gpu_bits: np.ndarray, ref: np.ndarray, what: str, max_frac:
     assert frac <= max_frac, f"{what}: {frac:.3e} of elements differ"
 
 
-def expected_schedule(tiles) -> np.ndarray:
-    """The block map's fourth column: tile indices, tallest tile first, equal heights
-    in tile order (the order the grouped GEMMs take the tiles in)."""
+def expected_schedule(tiles, block_m: int = 128, xcds: int = 8) -> np.ndarray:
+    """The block map's fourth column (the order the grouped GEMMs take the tiles in,
+    position i going to XCD i % xcds).
+
+    Positions 0 .. F-1 hold the F full tiles (block_m rows). Taken in tile order,
+    they are split into xcds consecutive runs whose lengths differ by at most one
+    (the longer runs first), and the r-th tile of run x sits at position
+    r * xcds + x, so every XCD gets a contiguous run. The partial tiles follow,
+    tallest first, equal heights in tile order."""
     tiles = np.asarray(tiles)
     heights = tiles[:, 2] - tiles[:, 1]
-    return np.array(sorted(range(len(tiles)), key=lambda i: (-int(heights[i]), i)), dtype=np.int64)
+    full = [i for i in range(len(tiles)) if heights[i] == block_m]
+    runs = np.array_split(np.array(full, dtype=np.int64), xcds)
+    sched = np.full(len(tiles), -1, dtype=np.int64)
+    for x, run in enumerate(runs):
+        for r, t in enumerate(run):
+            sched[r * xcds + x] = t
+    partial = sorted((i for i in range(len(tiles)) if heights[i] < block_m),
+                     key=lambda i: (-int(heights[i]), i))
+    sched[len(full):] = partial
+    assert sorted(sched.tolist()) == list(range(len(tiles)))
+    return sched
 
 
 def fill_expert_cache(weights, experts, cache, threads: int = 8):
