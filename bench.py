@@ -48,9 +48,10 @@ def expert_bytes(d, f):
     return 3 * d * f // 2 + 3 * d * f // 64 * 4
 
 
-# sources the grouped GEMM kernels are compiled from
+# sources the grouped GEMM kernels are compiled from, and the one that builds the
+# tile schedule they follow (which XCD reads which expert's weights)
 GEMM_SOURCES = [os.path.join("bit_quantized_grouped_router_amd", "csrc", n)
-                for n in ("moe_ffn.hip", "moe_device.h", "moe_launch.h")]
+                for n in ("moe_ffn.hip", "moe_device.h", "moe_launch.h", "moe_permute.hip")]
 
 
 def sources_hash(paths):

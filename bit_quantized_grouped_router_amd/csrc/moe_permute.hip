@@ -94,14 +94,24 @@ __device__ __forceinline__ int block_inclusive_scan(int v, int *wave_tot) {
 // x + 2 kXcds, ...: each XCD gets consecutive tiles, so a hot expert's full
 // tiles share one XCD's L2 instead of every XCD fetching that expert's
 // weights. Each XCD still receives the same positions, hence the same number
-// of tiles of each height. Position of full tile p (0 <= p < nfull):
-__device__ __forceinline__ int full_tile_position(int p, int nfull) {
-  const int q = nfull / kXcds, rem = nfull % kXcds;
-  const int big = rem * (q + 1);  // tiles in the longer runs
-  if (p < big) return kXcds * (p % (q + 1)) + p / (q + 1);
-  const int p2 = p - big;  // here q >= 1, since p < nfull
-  return kXcds * (p2 % q) + rem + p2 / q;
-}
+// of tiles of each height.
+// Run x and place r in it of full tile p (0 <= p < nfull); the next tile is
+// at r + 1 of the same run, or at 0 of run x + 1 once r reaches its length.
+struct FullRuns {
+  int q, rem;  // run length nfull / kXcds; the first rem runs are one longer
+  __device__ explicit FullRuns(int nfull) : q(nfull / kXcds), rem(nfull % kXcds) {}
+  __device__ int len(int x) const { return q + (x < rem ? 1 : 0); }
+  __device__ void locate(int p, int &x, int &r) const {
+    const int big = rem * (q + 1);  // tiles in the longer runs
+    if (p < big) {
+      x = p / (q + 1);
+      r = p - x * (q + 1);
+    } else {  // here q >= 1, since p < nfull
+      x = rem + (p - big) / q;
+      r = p - big - (x - rem) * q;
+    }
+  }
+};
 constexpr int kMaxGroups = kMaxExperts + 1;
 constexpr int kGroupWords = (kMaxGroups + 31) / 32;
 
@@ -180,9 +190,21 @@ __device__ void write_tile_map(PlaceLds &L, int c, int c_incl, int T, int E, int
   if (e < kBlockM - 1) L.u.m.hstart[hgt] = nfull + hc_incl - hc;
   __syncthreads();
   // schedule entries: full routed tiles, full shared tiles, partial tiles
+  const FullRuns runs(nfull);
+  if (e < E && nf > 0) {
+    // this expert's full tiles fbase .. fbase + nf - 1: located once, then
+    // stepped through the runs
+    int x, r;
+    runs.locate(fbase, x, r);
+    for (int i = 0; i < nf; ++i) {
+      tile_map[4 * (size_t)(kXcds * r + x) + 3] = tbase + i;
+      if (++r == runs.len(x)) {
+        ++x;
+        r = 0;
+      }
+    }
+  }
   if (e < E) {
-    for (int i = 0; i < nf; ++i)
-      tile_map[4 * (size_t)full_tile_position(fbase + i, nfull) + 3] = tbase + i;
     const int r = c % kBlockM;
     if (r) {
       int rank = __popc(L.u.m.hmask[r][e >> 5] & ((1u << (e & 31)) - 1u));
@@ -190,8 +212,11 @@ __device__ void write_tile_map(PlaceLds &L, int c, int c_incl, int T, int E, int
       tile_map[4 * (size_t)(L.u.m.hstart[r] + rank) + 3] = tbase + nf;
     }
   }
-  for (int i = e; i < T / kBlockM; i += kPlaceThreads)
-    tile_map[4 * (size_t)full_tile_position(L.routed_full + i, nfull) + 3] = rbase + i;
+  for (int i = e; i < T / kBlockM; i += kPlaceThreads) {
+    int x, r;
+    runs.locate(L.routed_full + i, x, r);
+    tile_map[4 * (size_t)(kXcds * r + x) + 3] = rbase + i;
+  }
   if (e == 0 && T % kBlockM) {
     const int r = T % kBlockM;
     int rank = 0;
