@@ -396,3 +396,49 @@ def test_tall_groups_from_repeated_ids(cfg):
     ref = dict(offsets=offsets, sorted_token=sorted_token)
     check_bf16_close(host_bits(h), h_ref, "h", max_frac=0.02, slack=_h_slack(cfg, inp, ref))
     check_y(y.cpu().numpy(), y_ref)
+
+
+# Routing built so that every expert a token block picks gets exactly 128 rows: token
+# block b (128 tokens) picks experts k*b .. k*b + k - 1, and the tokens past the last
+# whole block pick the next k experts. The full tiles F (routed, then the shared
+# expert's) then fall on each side of the XCD runs' edge cases: fewer than 8, exactly
+# 8, one and two past a multiple of 8, with and without partial tiles after them.
+FULL_RUNS = [
+    ("runs_f7_t128_k6", 128, 6, 8, 126),    # 6 + 1 full tiles: seven runs of one
+    ("runs_f8_t128_k7", 128, 7, 8, 127),    # 7 + 1: one tile per run
+    ("runs_f9_t128_k8", 128, 8, 16, 128),   # 8 + 1: run 0 holds two
+    ("runs_f18_t293_k8", 293, 8, 32, 129),  # 16 + 2, then nine 37-row tiles
+]
+
+
+@pytest.mark.parametrize("case", FULL_RUNS, ids=lambda c: c[0])
+def test_schedule_runs_of_full_tiles(case):
+    name, T, k, E, seed = case
+    say(f"[full-tile runs] {name}")
+    cfg = G.small_config(name, T=T, d=128, f=64, E=E, k=k, seed=seed)
+    inp = dict(G.make_layer_inputs(cfg))
+    logits = np.asarray(inp["logits"], dtype=np.float32) * np.float32(0.01)
+    for t in range(T):
+        b = t // 128
+        logits[t, [(k * b + j) % E for j in range(k)]] += np.float32(4.0 + 0.1 * np.arange(k))
+    inp["logits"] = logits
+    ref = O.layer_forward(inp["x"], logits, inp["weights"], k, BM=M.moe_block_m())
+    counts = ref["counts"]
+    assert sorted(set(counts.tolist()) - {0}) == sorted({128} | ({T % 128} - {0}))
+    dm, x, lg, w = upload(inp)
+    ids, wts = M.moe_route(lg, k)
+    perm = M.moe_permute(dm, ids)
+    h, o_r, o_sh = M.moe_expert_ffn_w4(dm, x, w, perm["sorted_token"], perm["tile_map"],
+                                       perm["num_tiles"])
+    y = M.moe_unpermute_combine(dm, o_r, o_sh, wts, perm["row_of"])
+    torch.cuda.synchronize()
+    assert np.array_equal(ids.cpu().numpy(), ref["ids"])
+    p = {kk: v.cpu().numpy() for kk, v in perm.items()}
+    n = int(p["num_tiles"][0])
+    assert n == len(ref["tiles"])
+    assert np.array_equal(p["tile_map"][:n, :3], ref["tiles"])
+    sched = expected_schedule(ref["tiles"])
+    assert np.array_equal(p["tile_map"][:n, 3], sched)
+    full = int(((ref["tiles"][:, 2] - ref["tiles"][:, 1]) == 128).sum())
+    assert full == {126: 7, 127: 8, 128: 9, 129: 18}[seed]
+    check_y(y.cpu().numpy(), ref["y"])
